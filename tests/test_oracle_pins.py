@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it checks.  None of them re-types the oracle's own
+formula: they compare it with worked examples from the pages, closed forms
+derived by hand, brute force, an independent least-squares solve, explicit
+sub-matrix inverses, or invariances.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import gptq_ref as ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _correlated_x(rng, n, d, mix=0.6):
+    """Token-major inputs with strongly correlated features."""
+    base = rng.standard_normal((n, d))
+    common = rng.standard_normal((n, 1))
+    return base * (1 - mix) + common * mix * rng.uniform(0.5, 1.5, size=(1, d))
+
+
+# --- P1: the ruler example ("What quantization is, and why anyone bothers") ---
+def test_grid_example_from_page():
+    g = _golden("grid_example.json")
+    scale, zero, _ = ref.fit_ruler(np.array([[g["row_min"], g["row_max"]]]), g["bits"])
+    # fp32 decision arithmetic: 0.08 to within one fp32 ulp.
+    assert abs(float(scale[0]) - g["scale"]) <= np.spacing(np.float32(g["scale"]))
+    assert zero[0] == g["zero_tick"]
+    ticks = ref.dequantize(np.arange(16), scale[0], zero[0])
+    np.testing.assert_allclose(ticks, g["ticks"], atol=1e-6)
+    # 0.0 is exactly one of the ticks.
+    assert ref.dequantize(g["zero_tick"], scale[0], zero[0]) == 0.0
+    q, _ = ref.round_to_grid(np.array(g["ticks"]), scale[0], zero[0], g["bits"])
+    np.testing.assert_array_equal(q, np.arange(16))
+
+
+def test_grid_range_includes_zero_and_clamps():
+    # All-positive row: the range is stretched down to 0, so the zero tick is 0.
+    scale, zero, _ = ref.fit_ruler(np.array([[0.3, 0.6, 0.9]]), 4)
+    assert zero[0] == 0 and np.isclose(scale[0], 0.9 / 15, rtol=1e-6)
+    # All-negative row: zero sits on the top tick.
+    scale, zero, _ = ref.fit_ruler(np.array([[-0.3, -0.9]]), 3)
+    assert zero[0] == 7
+    # A value past the end of the ruler clamps to the end tick.
+    q, _ = ref.round_to_grid(np.array([5.0, -5.0]), np.float32(0.1), 3.0, 3)
+    np.testing.assert_array_equal(q, [7, 0])
+    # Exact midpoints round half to even.
+    q, _ = ref.round_to_grid(np.array([0.25, 0.75]), np.float32(0.5), 0.0, 4)
+    np.testing.assert_array_equal(q, [0, 2])
+
+
+# --- P2: H = 2 X X^T is the Hessian of the output damage ("Measuring damage") ---
+def test_hessian_matches_finite_differences():
+    rng = np.random.default_rng(2)
+    n, d = 50, 5
+    X = rng.standard_normal((n, d))
+    w0 = rng.standard_normal(d)
+
+    def damage(w):
+        y = X @ (w - w0)
+        return float(y @ y)
+
+    h = 1e-2
+    fd = np.zeros((d, d))
+    w = w0 + rng.standard_normal(d) * 0.1
+    I = np.eye(d)
+    for i in range(d):
+        for j in range(d):
+            fd[i, j] = (damage(w + h * I[i] + h * I[j]) - damage(w + h * I[i] - h * I[j])
+                        - damage(w - h * I[i] + h * I[j]) + damage(w - h * I[i] - h * I[j])) / (4 * h * h)
+    H = ref.hessian(X)
+    assert np.linalg.norm(H - fd) / np.linalg.norm(H) <= 1e-6
+
+
+def test_hessian_chunking_and_loss_forms_agree():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((1000, 7)).astype(np.float32)
+    H1 = ref.hessian(X, chunk=1 << 20)
+    H2 = ref.hessian(X, chunk=37)
+    np.testing.assert_allclose(H1, H2, rtol=1e-12, atol=1e-9)
+    W0 = rng.standard_normal((3, 7))
+    Wh = W0 + 0.01 * rng.standard_normal((3, 7))
+    a = ref.layer_loss(W0, Wh, H1)
+    b = ref.layer_loss_from_x(W0, Wh, X)
+    assert abs(a - b) <= 1e-10 * b
+
+
+# --- P3: the two-weight example ("Measuring damage where it matters") ---
+def test_two_weight_example_undamped_repair_is_exact():
+    g = _golden("two_weight_example.json")
+    rng = np.random.default_rng(4)
+    x1 = rng.standard_normal(1000)
+    X = np.stack([x1, x1], axis=1)
+    w = np.array([g["w1"], g["w2"]])
+    unrep = np.array([g["w1_forced"], g["w2"]])
+    err_unrep = ref.layer_loss_from_x(w[None], unrep[None], X)
+    assert np.isclose(err_unrep, g["error"] ** 2 * np.sum(x1 * x1), rtol=1e-12)
+    fixed = ref.lstsq_repair(w, X, 0, g["w1_forced"])
+    assert np.isclose(fixed[1], g["w2_repaired"], atol=1e-12)
+    err_fixed = ref.layer_loss_from_x(w[None], fixed[None], X)
+    assert err_fixed <= 1e-25 * err_unrep
+
+
+def test_two_weight_example_damped_pipeline_closed_form():
+    # With x2 = x1, H = 2a[[1,1],[1,1]]; 1 % damping of the mean diagonal gives
+    # H_d = 2a[[1+p, 1],[1, 1+p]], whose OBS repair moves w2 by e1/(1+p).
+    # The output error left before w2's own rounding is therefore
+    # (p/(1+p))^2 of the unrepaired one (derived by hand from the 2x2 inverse).
+    p = _golden("damping.json")["percdamp"]
+    g = _golden("two_weight_example.json")
+    rng = np.random.default_rng(5)
+    x1 = rng.standard_normal(1000)
+    X = np.stack([x1, x1], axis=1)
+    W0 = np.array([[g["w1"], g["w2"]]])
+    out = ref.gptq_quantize(W0, ref.hessian(X), bits=4, percdamp=p)
+    e1 = W0[0, 0] - out["w_hat"][0, 0]
+    assert abs(e1) > 1e-4
+    w2_turn = out["pre_round"][0, 1]
+    assert np.isclose(w2_turn - W0[0, 1], e1 / (1 + p), rtol=1e-12)
+    partial = np.array([[out["w_hat"][0, 0], w2_turn]])
+    ratio = ref.layer_loss_from_x(W0, partial, X) / (e1 * e1 * np.sum(x1 * x1))
+    assert np.isclose(ratio, (p / (1 + p)) ** 2, rtol=1e-9)
+    assert np.isclose((p / (1 + p)) ** 2, 9.80296e-5, rtol=1e-5)
+
+
+def test_singular_without_damping_is_an_error():
+    x1 = np.random.default_rng(6).standard_normal(100)
+    X = np.stack([x1, x1], axis=1)
+    with pytest.raises(ref.NotPositiveDefinite):
+        ref.gptq_quantize(np.array([[0.1, 0.2]]), ref.hessian(X), bits=4, percdamp=0.0)
+
+
+# --- P4: OBS formula equals brute-force least squares ("The repair rule") ---
+def test_obs_repair_equals_least_squares():
+    rng = np.random.default_rng(7)
+    for trial in range(5):
+        X = _correlated_x(rng, 40, 6)
+        w = rng.standard_normal(6)
+        q = trial % 6
+        value = np.round(w[q] * 4) / 4
+        a = ref.obs_repair(w, ref.hessian(X), q, value)
+        b = ref.lstsq_repair(w, X, q, value)
+        assert a[q] == pytest.approx(value, abs=1e-15)
+        assert np.max(np.abs(a - b)) <= 1e-13 * max(1.0, np.max(np.abs(w)))
+
+
+# --- P5: correlation rho ("The repair rule", two correlated inputs) ---
+@pytest.mark.parametrize("rho", [0.0, 0.3, 0.9, -0.5])
+@pytest.mark.parametrize("damp", [0.0, 0.01])
+def test_correlated_pair_absorption_and_damage(rho, damp):
+    rng = np.random.default_rng(8)
+    n = 256
+    x1 = rng.standard_normal(n)
+    z = rng.standard_normal(n)
+    z -= (z @ x1) / (x1 @ x1) * x1            # exactly orthogonal to x1
+    z *= np.linalg.norm(x1) / np.linalg.norm(z)
+    x2 = rho * x1 + np.sqrt(1 - rho * rho) * z  # sample correlation exactly rho
+    X = np.stack([x1, x2], axis=1)
+    H = ref.hessian(X)
+    H[np.arange(2), np.arange(2)] += damp * np.mean(np.diag(H))
+    w = np.array([0.4, -0.2])
+    e = 0.05
+    rep = ref.obs_repair(w, H, 0, w[0] - e)
+    assert rep[1] - w[1] == pytest.approx(rho * e / (1 + damp), abs=1e-14)
+    if damp == 0.0:
+        unrep = np.array([w[0] - e, w[1]])
+        dmg_rep = ref.layer_loss_from_x(w[None], rep[None], X)
+        dmg_unrep = ref.layer_loss_from_x(w[None], unrep[None], X)
+        assert dmg_rep / dmg_unrep == pytest.approx(1 - rho * rho, abs=1e-12)
+
+
+# --- P6: the Cholesky factor holds every shrinking inverse ("From one repair to a whole model") ---
+def test_upper_factor_rows_are_the_shrinking_inverses():
+    rng = np.random.default_rng(9)
+    d = 7
+    A = rng.standard_normal((d, 3 * d))
+    Hd = A @ A.T + 0.1 * np.eye(d)
+    U = ref.upper_cholesky_of_inverse(Hd)
+    assert np.allclose(np.tril(U, -1), 0)
+    np.testing.assert_allclose(U.T @ U, np.linalg.inv(Hd), rtol=1e-10, atol=1e-12)
+    for q in range(d):
+        Finv = np.linalg.inv(Hd[q:, q:])       # inverse restricted to the free set
+        assert U[q, q] ** 2 == pytest.approx(Finv[0, 0], rel=1e-10)
+        np.testing.assert_allclose(U[q, q:] / U[q, q], Finv[:, 0] / Finv[0, 0], rtol=1e-9, atol=1e-12)
+
+
+def test_oracle_steps_match_repeated_obs_repairs():
+    # Column-by-column GPTQ = quantize one weight, OBS-repair the rest with the
+    # inverse of the still-free sub-matrix, repeat (the pre-GPTQ formulation
+    # with a fixed order).  Check the pre-rounding values step by step.
+    rng = np.random.default_rng(10)
+    d = 6
+    X = _correlated_x(rng, 60, d)
+    W0 = rng.standard_normal((1, d)) * 0.1
+    out = ref.gptq_quantize(W0, ref.hessian(X), bits=3, percdamp=0.01)
+    Hd, _, _, _ = ref.prepare(ref.hessian(X), 0.01)
+    w = W0[0].copy()
+    for j in range(d):
+        assert w[j] == pytest.approx(out["pre_round"][0, j], abs=1e-12)
+        sub = ref.obs_repair(w[j:], Hd[j:, j:], 0, out["w_hat"][0, j])
+        w[j:] = sub
+
+
+# --- P7: H = c I reduces GPTQ to round-to-nearest ("The repair rule", rho = 0) ---
+@pytest.mark.parametrize("groupsize", [-1, 16, 32])
+@pytest.mark.parametrize("bits", [3, 4])
+def test_identity_hessian_is_round_to_nearest(groupsize, bits):
+    rng = np.random.default_rng(11)
+    r, c = 17, 64
+    W0 = rng.standard_normal((r, c)) * 0.02
+    X = 3.0 * np.eye(c)                       # c tokens, one per input
+    out = ref.gptq_quantize(W0, ref.hessian(X), bits=bits, groupsize=groupsize)
+    codes, w_hat = ref.rtn(W0, bits, groupsize)
+    np.testing.assert_array_equal(out["codes"], codes)
+    np.testing.assert_array_equal(out["w_hat"], w_hat)
+
+
+# --- P8: lazy blocks equal the plain column loop ("From one repair to a whole model") ---
+@pytest.mark.parametrize("B,groupsize", [(128, -1), (1, -1), (7, -1), (32, 64), (128, 32), (32, 32), (64, 128)])
+def test_lazy_batches_equal_plain_loop(B, groupsize):
+    rng = np.random.default_rng(12)
+    r, c = 9, 300 if groupsize <= 0 else 256
+    X = _correlated_x(rng, 400, c)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    H = ref.hessian(X)
+    a = ref.gptq_quantize(W0, H, bits=4, groupsize=groupsize)
+    b = ref.gptq_quantize(W0, H, bits=4, groupsize=groupsize, blocksize=B)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_allclose(a["row_loss"], b["row_loss"], rtol=1e-12)
+    np.testing.assert_allclose(a["pre_round"], b["pre_round"], rtol=1e-10, atol=1e-14)
+
+
+# --- P9: the tracked losses add up to the damped quadratic form ---
+def test_loss_bookkeeping_sums_to_quadratic_form():
+    rng = np.random.default_rng(13)
+    r, c = 11, 40
+    X = _correlated_x(rng, 200, c)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    H = ref.hessian(X)
+    for act_order in (False, True):
+        out = ref.gptq_quantize(W0, H, bits=3, groupsize=8, act_order=act_order)
+        Hd, perm, _, lam = ref.prepare(H, 0.01, act_order)
+        D = (out["w_hat"] - W0)[:, perm]
+        quad = 0.5 * np.einsum("ri,ij,rj->r", D, Hd, D)
+        np.testing.assert_allclose(out["row_loss"], quad, rtol=1e-9)
+        direct = ref.layer_loss_from_x(W0, out["w_hat"], X) + 0.5 * lam * np.sum(D * D)
+        assert np.sum(out["row_loss"]) == pytest.approx(direct, rel=1e-9)
+
+
+# --- P10: tiny layers against the exhaustive optimum ---
+def test_tiny_layers_against_brute_force():
+    rng = np.random.default_rng(14)
+    ratios_gptq, ratios_rtn = [], []
+    for _ in range(30):
+        d = int(rng.integers(3, 6))
+        X = _correlated_x(rng, 24, d, mix=0.8)
+        w0 = rng.standard_normal(d) * 0.1
+        out = ref.gptq_quantize(w0[None], ref.hessian(X), bits=3, percdamp=0.01)
+        scale, zero = out["scales"][0, 0], out["zeros"][0, 0]
+        best_codes, best = ref.brute_force_row(w0, X, scale, zero, 3)
+        rtn_codes, rtn_hat = ref.rtn(w0[None], 3)
+        g_obj = ref.layer_loss_from_x(w0[None], out["w_hat"], X)
+        r_obj = ref.layer_loss_from_x(w0[None], rtn_hat, X)
+        assert best <= g_obj * (1 + 1e-12) and best <= r_obj * (1 + 1e-12)
+        ratios_gptq.append(g_obj / best)
+        ratios_rtn.append(r_obj / best)
+    # Compensation must help on correlated inputs; a flipped sign makes it hurt.
+    assert np.mean(ratios_gptq) < np.mean(ratios_rtn)
+    assert np.median(ratios_gptq) < 1.5
+
+
+# --- P11: act-order is GPTQ on the explicitly permuted problem ("Paper vs. code") ---
+def test_act_order_is_explicit_permutation():
+    rng = np.random.default_rng(15)
+    r, c = 8, 48
+    X = _correlated_x(rng, 200, c) * rng.uniform(0.1, 3.0, size=(1, c))
+    X[:, 5] = X[:, 9]                          # a tie in diag(H)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    H = ref.hessian(X)
+    a = ref.gptq_quantize(W0, H, bits=4, groupsize=16, act_order=True)
+    perm = a["perm"]
+    dg = np.diag(H)[perm]
+    assert np.all(np.diff(dg) <= 0)
+    ties = np.flatnonzero(np.diff(dg) == 0)
+    assert all(perm[t] < perm[t + 1] for t in ties) and len(ties) >= 1
+    b = ref.gptq_quantize(W0[:, perm], H[np.ix_(perm, perm)], bits=4, groupsize=16)
+    np.testing.assert_array_equal(a["codes"][:, perm], b["codes"])
+    np.testing.assert_array_equal(a["scales"], b["scales"])
+    np.testing.assert_array_equal(a["g_idx"][perm], np.arange(c) // 16)
+
+
+# --- P12: one group spanning the row equals the per-row ruler ---
+def test_single_group_equals_per_row():
+    rng = np.random.default_rng(16)
+    r, c = 10, 64
+    X = _correlated_x(rng, 300, c)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    H = ref.hessian(X)
+    a = ref.gptq_quantize(W0, H, bits=4, groupsize=-1)
+    b = ref.gptq_quantize(W0, H, bits=4, groupsize=c)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(a["scales"], b["scales"])
+
+
+# --- P13: invariances (H shared by every row; scale of H irrelevant) ---
+def test_scaling_inputs_and_permuting_rows():
+    rng = np.random.default_rng(17)
+    r, c = 12, 40
+    X = _correlated_x(rng, 120, c)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    a = ref.gptq_quantize(W0, ref.hessian(X), bits=4, groupsize=8)
+    b = ref.gptq_quantize(W0, ref.hessian(2.0 * X), bits=4, groupsize=8)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(a["w_hat"], b["w_hat"])
+    rp = rng.permutation(r)
+    p = ref.gptq_quantize(W0[rp], ref.hessian(X), bits=4, groupsize=8)
+    np.testing.assert_array_equal(p["codes"], a["codes"][rp])
+    np.testing.assert_array_equal(p["row_loss"], a["row_loss"][rp])
+
+
+# --- dead inputs ("Paper vs. code": silent inputs zeroed) ---
+def test_dead_inputs_zeroed_and_per_row_ruler_sees_original():
+    rng = np.random.default_rng(18)
+    r, c = 6, 16
+    X = _correlated_x(rng, 100, c)
+    X[:, 3] = 0.0
+    W0 = rng.standard_normal((r, c)) * 0.02
+    W0[0, 3] = 1.0                              # dominates row 0's range
+    out = ref.gptq_quantize(W0, ref.hessian(X), bits=4)
+    assert out["dead"][3] and out["dead"].sum() == 1
+    assert np.all(out["w_hat"][:, 3] == 0.0)
+    np.testing.assert_array_equal(out["codes"][:, 3], out["zeros"][:, 0])
+    s_row, _, _ = ref.fit_ruler(W0[:1], 4)
+    assert out["scales"][0, 0] == s_row[0]      # range still includes the 1.0
+    # The dead diagonal is set to 1 before damping, so it enters the mean.
+    H = ref.hessian(X)
+    assert out["lam"] == pytest.approx(0.01 * (np.trace(H) + 1.0) / c, rel=1e-14)
+
+
+# --- tie replay adjudication ---
+def test_tie_replay_adopts_only_near_ties():
+    rng = np.random.default_rng(19)
+    r, c = 6, 32
+    X = _correlated_x(rng, 100, c)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    H = ref.hessian(X)
+    base = ref.gptq_quantize(W0, H, bits=4)
+    same = ref.TieReplay(base["codes_proc"], base["zeros"])
+    again = ref.gptq_quantize(W0, H, bits=4, replay=same)
+    assert same.hard == 0 and same.near_ties == 0
+    np.testing.assert_array_equal(again["codes"], base["codes"])
+    # Shift one code far from any midpoint: counted as hard, not adopted.
+    bad = base["codes_proc"].copy()
+    j = 5
+    t = base["pre_round"][2, j] / base["scales"][2, 0]
+    if abs(t - np.floor(t) - 0.5) > 0.01:
+        bad[2, j] = (bad[2, j] + 3) % 16
+        rep = ref.TieReplay(bad, base["zeros"])
+        ref.gptq_quantize(W0, H, bits=4, replay=rep)
+        assert rep.hard == 1
+
+
+# --- P14: packed layout (this project's layout; the pages fix none) ---
+def test_pack_layout_closed_forms_and_round_trip():
+    # 4 bits: code k of a word sits in hex digit k.
+    w4 = ref.pack_codes(np.arange(8)[None], 4)
+    assert int(w4[0, 0]) == 0x76543210
+    # 3 bits: codes k % 8 for k = 0..31 over 96 little-endian bits; the 24-bit
+    # pattern 0xFAC688 (codes 0..7) repeats four times.
+    w3 = ref.pack_codes((np.arange(32) % 8)[None], 3)
+    assert [int(x) for x in w3[0]] == [0x88FAC688, 0xC688FAC6, 0xFAC688FA]
+    rng = np.random.default_rng(20)
+    for bits, c in ((4, 64), (3, 96)):
+        codes = rng.integers(0, 2 ** bits, size=(5, c))
+        words = ref.pack_codes(codes, bits)
+        assert words.nbytes == 5 * c * bits // 8
+        np.testing.assert_array_equal(ref.unpack_codes(words, bits, c), codes)
