@@ -1,0 +1,241 @@
+"""Throughput of the GPTQ layer quantizer on one MI355X.
+
+One step = the whole path for one layer of the named workload, with the
+weights and the calibration activations already resident in HBM:
+    H = 0;  H += 2 X^T X  (gptq_hessian_accumulate)
+    U = chol_upper((H + damp)^{-1})  (gptq_prepare)
+    codes, rulers = GPTQ column loop  (gptq_quantize_layer)
+    packed words  (gptq_pack)
+Prints ONE JSON line: weights/s for the whole layer (value), seconds per layer,
+Hessian TFLOP/s, per-stage milliseconds, the roofline of the dominant kernel
+(the Hessian SYRK, timed with HIP events on the stream it runs on), and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+    python bench.py --copy-probe      # plain copy of known size (PMC calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sec per layer & weights/s for GPTQ 4-bit g128 on 4096×4096; Hessian TFLOP/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_syrk16_{workload}.json")
+SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "syrk.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per SYRK launch from committed PMC counters, or None when the
+    kernel source changed since they were taken."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha256") != source_hash(SYRK_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} copies of {nbytes} bytes (read {nbytes}, write {nbytes} each)")
+
+
+def cpu_baseline(W_dev, X_dev, w, tokens_sample=16384, rows_sample=128):
+    """The oracle as it stands, on a bounded sample, extrapolated to one layer."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import gptq_ref as ref
+
+    X = X_dev[:tokens_sample].float().cpu().numpy()
+    W = W_dev.float().cpu().numpy()
+    t0 = time.perf_counter()
+    H = ref.hessian(X)
+    t_h = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Hd, perm, dead, lam = ref.prepare(H, w.percdamp, w.act_order)
+    U = ref.upper_cholesky_of_inverse(Hd)
+    t_p = time.perf_counter() - t0
+    rows = np.arange(rows_sample)
+    t0 = time.perf_counter()
+    ref.gptq_quantize(W[rows].astype(np.float64), H, w.bits, w.groupsize, w.percdamp, w.act_order, U=U)
+    t_q = time.perf_counter() - t0
+    scale_h = w.tokens / tokens_sample
+    scale_q = w.rows / rows_sample
+    sec_layer = t_h * scale_h + t_p + t_q * scale_q
+    threads = [p.get("num_threads", 0) for p in threadpool_info()]
+    cores = max(threads) if threads else 1
+    return {
+        "value": (w.rows * w.cols) / sec_layer,
+        "unit": "weights/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"H on {tokens_sample} of {w.tokens} tokens (x{scale_h:g}), U on the full {w.cols}^2 H, "
+                   f"column loop on {rows_sample} of {w.rows} rows (x{scale_q:g}); linear extrapolation; "
+                   f"measured s: H {t_h:.2f}, prepare {t_p:.2f}, loop {t_q:.2f}"),
+        "sec_per_layer_extrapolated": sec_layer,
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama7b_attn_4096x4096")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the quantizer's path runs on a single MI355X here "
+              "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_probe:
+        copy_probe()
+        return 0
+
+    from post_weight_quantization_23_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_23_amd import build as b
+        b.build()
+    import post_weight_quantization_23_amd as q
+    from synth import inputs as S
+
+    w = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {w.name}: W {w.rows}x{w.cols} {w.w_dtype}, X {w.tokens}x{w.cols} {w.x_dtype}")
+    W, X = S.workload_device(w, device=dev)
+    torch.cuda.synchronize()
+
+    d, r, c = w.cols, w.rows, w.cols
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    G = (c + w.groupsize - 1) // w.groupsize if w.groupsize > 0 else 1
+    out = {
+        "codes": torch.empty((r, c), dtype=torch.uint8, device=dev),
+        "scales": torch.empty((r, G), dtype=torch.float32, device=dev),
+        "zeros": torch.empty((r, G), dtype=torch.int32, device=dev),
+        "g_idx": torch.empty(c, dtype=torch.int32, device=dev),
+        "row_loss": torch.empty(r, dtype=torch.float32, device=dev),
+    }
+    packed = torch.empty((r, c * w.bits // 32), dtype=torch.uint32, device=dev)
+    ws_h, ws_p, ws_q = q.Workspace(), q.Workspace(), q.Workspace()
+
+    def step(ev):
+        ev[0].record()
+        H.zero_()
+        q.hessian_accumulate(H, X, ws=ws_h)
+        ev[1].record()
+        perm, dead, info = q.prepare(H, w.percdamp, w.act_order, check=False, ws=ws_p)
+        ev[2].record()
+        q.quantize_layer(W, H, perm, dead, bits=w.bits, groupsize=w.groupsize, blocksize=w.blocksize,
+                         ws=ws_q, out=out)
+        ev[3].record()
+        q.pack(out["codes"], w.bits, out=packed)
+        ev[4].record()
+        return info
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for _ in range(args.warmup):
+        info = step(mk())
+    torch.cuda.synchronize()
+    if args.warmup and int(info.item()) != 0:
+        raise RuntimeError(f"prepare reported info = {int(info.item())}")
+
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage = {"hessian": [], "prepare": [], "quantize": [], "pack": [], "step": []}
+    for ev in evs:
+        stage["hessian"].append(ev[0].elapsed_time(ev[1]))
+        stage["prepare"].append(ev[1].elapsed_time(ev[2]))
+        stage["quantize"].append(ev[2].elapsed_time(ev[3]))
+        stage["pack"].append(ev[3].elapsed_time(ev[4]))
+        stage["step"].append(ev[0].elapsed_time(ev[4]))
+    avg = {k: sum(v) / len(v) for k, v in stage.items()}
+    ms_step = wall * 1e3 / args.steps
+    sec_layer = ms_step / 1e3
+    flops_h = d * (d + 1) * w.tokens
+    hess_tflops = flops_h / (avg["hessian"] / 1e3) / 1e12
+    peak = PEAK_FP16_TFLOPS if w.x_dtype == "float16" else PEAK_BF16_TFLOPS
+    traffic = load_traffic(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": (r * c) / sec_layer,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.x_dtype == "bfloat16" else ("fp16" if w.x_dtype == "float16" else "f32"),
+        "data": "synthetic (seeded; N(0,0.02^2) weights, Student-t(4) activations with outlier channels)",
+        "config": {"workload": w.name, "rows": r, "cols": c, "tokens": w.tokens, "bits": w.bits,
+                   "groupsize": w.groupsize, "blocksize": w.blocksize, "percdamp": w.percdamp,
+                   "act_order": w.act_order, "w_dtype": w.w_dtype, "x_dtype": w.x_dtype},
+        "sec_per_layer": sec_layer,
+        "hessian_tflops": hess_tflops,
+        "stage_ms": {k: round(v, 4) for k, v in avg.items()},
+        "roofline": {
+            "kernel": "syrk16_kernel (Hessian H += 2 X^T X)",
+            "bound": "mfma",
+            "achieved": hess_tflops,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": hess_tflops / peak,
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": flops_h,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(W, X, w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

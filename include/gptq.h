@@ -1,0 +1,182 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer quantizer.
+ *
+ * The method is the GPTQ layer-wise quantizer as described on the page
+ * "GPTQ, with the code open" (modelfoundations.com/notes/gptq):
+ *   - section "Measuring damage where it matters": H = 2 X X^T, one matrix
+ *     shared by every output row;
+ *   - section "Paper vs. code": H accumulated over calibration batches, inputs
+ *     that never fire ("dead") zeroed, 1 % of the mean diagonal added as
+ *     damping, full fp32 arithmetic, act-order, rulers per group of columns;
+ *   - section "From one repair to a whole model": the upper Cholesky factor of
+ *     the inverse of H drives every repair; columns are quantized in one fixed
+ *     order for all rows, in blocks of 128 whose repairs are applied at once
+ *     inside the block and deferred to one matrix product beyond it;
+ *   - section "What quantization is, and why anyone bothers": the asymmetric
+ *     min-max ruler, scale = (max - min)/(2^b - 1), the zero point rounded to
+ *     a whole tick, w_hat = scale * (q - zero).
+ *
+ * Conventions shared by every call:
+ *   - Every pointer argument that names an array is a DEVICE pointer (memory
+ *     allocated by the caller on the current HIP device) unless stated
+ *     otherwise.  Output-size pointers of the *_workspace_size queries are
+ *     HOST pointers.  The library allocates no memory of its own: scratch
+ *     space is a caller-provided workspace sized by the matching query.
+ *   - Matrices are row-major with an explicit leading dimension in ELEMENTS.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on that stream and never synchronise; results are valid once the
+ *     stream has reached the call.
+ *   - Every argument is validated on the host before anything is enqueued:
+ *     a call that returns an error has enqueued nothing.  GPTQ_EHIP reports a
+ *     failed kernel launch (gptq_last_error() carries HIP's message).
+ *   - Buffers passed to one call must not overlap unless stated.
+ *   - Calls are deterministic: the same inputs give bitwise-identical outputs
+ *     (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = 1,        /* null pointer, negative size, bad enum value      */
+  GPTQ_EDTYPE = 2,        /* dtype not supported by this call                 */
+  GPTQ_ESHAPE = 3,        /* inconsistent sizes / leading dimensions           */
+  GPTQ_EALIGN = 4,        /* a pointer or leading dimension is misaligned      */
+  GPTQ_EUNSUPPORTED = 5,  /* valid request outside what this build supports    */
+  GPTQ_EWORKSPACE = 6,    /* workspace missing or smaller than the query says */
+  GPTQ_EHIP = 7           /* a HIP launch failed                               */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
+
+/* ------------------------------------------------------------------------
+ * Hessian accumulation.  Page: "GPTQ, with the code open", section
+ * "Measuring damage where it matters" (H = 2 X X^T) and the "Paper vs. code"
+ * table (H built up over calibration batches).
+ *
+ *   H[i][j] += 2 * sum_t X[t][i] * X[t][j]      for 0 <= i <= j < d
+ *
+ * H      : d x d fp32, row-major, leading dimension d.  Only the upper
+ *          triangle including the diagonal is defined on return; entries
+ *          strictly below the diagonal are unspecified (they may be
+ *          overwritten).  The caller zeroes H once before the first batch;
+ *          repeated calls accumulate the raw sum (no running-mean rescale).
+ * X      : n_tok x d calibration inputs, token-major (one row per token),
+ *          row stride ldx >= d elements, dtype xt (GPTQ_BF16, GPTQ_F16 or
+ *          GPTQ_F32).  Products are formed exactly and summed in fp32.
+ *          bf16/fp16 X needs a 16-byte aligned pointer and ldx % 8 == 0
+ *          (GPTQ_EALIGN otherwise).  n_tok == 0 or d == 0 is a no-op.
+ * ws     : workspace of at least gptq_hessian_workspace_size() bytes
+ *          (may be NULL when that size is 0); 256-byte aligned.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_hessian_workspace_size(int64_t d, int64_t n_tok, gptq_dtype xt,
+                                        size_t* bytes);
+gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, gptq_dtype xt,
+                                    int64_t n_tok, int64_t ldx, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------
+ * Preparation of H.  Page: "GPTQ, with the code open", "Paper vs. code"
+ * (dead inputs, 1 % damping of the mean diagonal, act-order) and "From one
+ * repair to a whole model" (the Cholesky factor of the inverse).
+ *
+ * In order, on the device:
+ *   1. dead[j] = (H[j][j] == 0); such diagonals are set to 1;
+ *   2. if act_order: perm = indices sorted by H[j][j] descending, ties by
+ *      ascending index (a stable sort); else perm = identity.  H is
+ *      permuted symmetrically into processing order;
+ *   3. lambda = percdamp * mean(diag H); H[j][j] += lambda;
+ *   4. H is replaced by U, the upper triangular matrix with positive
+ *      diagonal and U^T U = H^{-1} (processing order).  The strictly lower
+ *      triangle is set to 0.
+ *
+ * H_to_U : d x d fp32 row-major (ld d), upper triangle read, U written.
+ * perm   : int32[d] out (processing position k -> original column perm[k]).
+ *          May be NULL only when act_order == 0.
+ * dead   : uint8[d] out, indexed by ORIGINAL column.
+ * info   : int32 out (device): 0 on success; k > 0 if the damped matrix is not
+ *          positive definite, k being the 1-based processing position of the
+ *          first failing pivot found; -1 if a diagonal entry is NaN or Inf.
+ *          U is undefined when info != 0.  The call itself cannot see info
+ *          (it does not synchronise): read it after the stream reaches it.
+ * ws     : workspace of at least gptq_prepare_workspace_size() bytes.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_prepare_workspace_size(int64_t d, int act_order, size_t* bytes);
+gptq_status gptq_prepare(float* H_to_U, int64_t d, float percdamp, int act_order,
+                         int32_t* perm, uint8_t* dead, int32_t* info, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Quantize one layer.  Page: "GPTQ, with the code open", sections "What
+ * quantization is" (ruler), "The repair rule" and "From one repair to a whole
+ * model" (the column loop, the per-weight loss (w - q)^2 / (2 d^2), blocks of
+ * `blocksize` columns with deferred repairs, rulers fitted before repairs),
+ * and "Paper vs. code" (groupsize, act-order, dead inputs).
+ *
+ * W        : r x c weights (one output per row), row stride ldw >= c, dtype
+ *            wt; read only.
+ * U        : c x c from gptq_prepare (processing order).
+ * perm     : int32[c] from gptq_prepare, or NULL for the identity order.
+ * dead     : uint8[c] from gptq_prepare (original order), or NULL (none).
+ * bits     : 2, 3, 4 or 8.
+ * groupsize: <= 0 -> one ruler per row, fitted on the original weights
+ *            before dead inputs are zeroed; > 0 -> one ruler per run of
+ *            `groupsize` columns in processing order, fitted when the loop
+ *            reaches the run's first column on the current (repaired) values.
+ *            The last run may be shorter than groupsize.  Requires
+ *            groupsize % blocksize == 0 or blocksize % groupsize == 0.
+ * blocksize: 1 .. 128 (columns whose repairs are applied immediately).
+ * codes    : r x c uint8 out, ORIGINAL column order, values 0 .. 2^bits - 1.
+ * scales   : r x n_groups fp32 out; zeros: r x n_groups int32 out, where
+ *            n_groups = groupsize > 0 ? ceil(c / groupsize) : 1, in
+ *            processing order of the runs.
+ * g_idx    : int32[c] out: run index of each ORIGINAL column (0 when
+ *            groupsize <= 0).
+ * W_hat    : r x c fp32 out (nullable), ORIGINAL column order,
+ *            scale * (code - zero).
+ * row_loss : fp32[r] out (nullable): sum over the row of (w - q)^2 / (2 U_jj^2).
+ * ws       : workspace of at least gptq_quantize_layer_workspace_size() bytes.
+ * Ties round half to even; the code is clamp(rne(w / scale) + zero, 0, 2^b-1);
+ * every decision (ruler and rounding) is taken in IEEE fp32.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_quantize_layer_workspace_size(int64_t r, int64_t c, int64_t blocksize,
+                                               size_t* bytes);
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t c,
+                                int64_t ldw, const float* U, const int32_t* perm,
+                                const uint8_t* dead, int bits, int64_t groupsize,
+                                int64_t blocksize, uint8_t* codes, float* scales,
+                                int32_t* zeros, int32_t* g_idx, float* W_hat,
+                                float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Pack codes into 32-bit words.  The pages only state that each weight is
+ * stored as the index of its tick ("What quantization is, and why anyone
+ * bothers"); the word layout is this library's:
+ *   bits == 4: 8 codes per word, code k of the word in bits 4k .. 4k+3;
+ *   bits == 3: 32 codes per 3 words, code k in bits 3k .. 3k+2 of the
+ *              little-endian 96-bit value (word 0 = bits 0..31), so codes 10
+ *              and 21 straddle two words.
+ * Packed along the input (column) axis, one output row at a time.
+ * codes  : r x c uint8 (values must fit in `bits`; higher bits are ignored).
+ * packed : r x ld_words uint32 out; ld_words >= c * bits / 32.
+ * Requires c % 8 == 0 (4-bit) or c % 32 == 0 (3-bit).
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
+                      int64_t ld_words, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* gptq_status_string(gptq_status s);
+/* Detail of the last failure on the calling thread (thread-local storage). */
+const char* gptq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_MI355X_H */

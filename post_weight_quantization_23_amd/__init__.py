@@ -1,0 +1,8 @@
+"""MI355X (gfx950) GPTQ layer quantizer: Hessian SYRK, damped inverse Cholesky
+factor, lazy-block quantize-and-repair, and int3/int4 packing, as hand-written
+HIP kernels behind the C ABI in include/gptq.h."""
+from .gptq import (GPTQError, NotPositiveDefinite, Workspace, hessian_accumulate, pack, prepare,
+                   quantize_layer)
+
+__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "Workspace",
+           "NotPositiveDefinite", "GPTQError"]

@@ -1,0 +1,73 @@
+"""ctypes loader for libgptq_mi355x.so (the C ABI in include/gptq.h).
+
+There is no fallback: if the library is missing or does not load, every entry
+point raises.  Build it with `python -m post_weight_quantization_23_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptq_mi355x.so")
+
+GPTQ_F32, GPTQ_BF16, GPTQ_F16 = 0, 1, 2
+STATUS = {0: "GPTQ_OK", 1: "GPTQ_EINVAL", 2: "GPTQ_EDTYPE", 3: "GPTQ_ESHAPE", 4: "GPTQ_EALIGN",
+          5: "GPTQ_EUNSUPPORTED", 6: "GPTQ_EWORKSPACE", 7: "GPTQ_EHIP"}
+
+# name -> (restype, argtypes), mirroring include/gptq.h
+_P = C.c_void_p
+_I64 = C.c_int64
+_SZ = C.c_size_t
+_SZP = C.POINTER(C.c_size_t)
+SIGNATURES = {
+    "gptq_hessian_workspace_size": (C.c_int, [_I64, _I64, C.c_int, _SZP]),
+    "gptq_hessian_accumulate": (C.c_int, [_P, _I64, _P, C.c_int, _I64, _I64, _P, _SZ, _P]),
+    "gptq_prepare_workspace_size": (C.c_int, [_I64, C.c_int, _SZP]),
+    "gptq_prepare": (C.c_int, [_P, _I64, C.c_float, C.c_int, _P, _P, _P, _P, _SZ, _P]),
+    "gptq_quantize_layer_workspace_size": (C.c_int, [_I64, _I64, _I64, _SZP]),
+    "gptq_quantize_layer": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _P, _P, _P, C.c_int, _I64, _I64,
+                                      _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "gptq_pack": (C.c_int, [_P, _I64, _I64, C.c_int, _P, _I64, _P]),
+    "gptq_status_string": (C.c_char_p, [C.c_int]),
+    "gptq_last_error": (C.c_char_p, []),
+}
+
+_lib = None
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn} -> {STATUS.get(status, status)}: {detail}")
+
+
+def load() -> C.CDLL:
+    """Load the HIP library once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m post_weight_quantization_23_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def call(name: str, *args) -> None:
+    """Call an entry point and raise GPTQError on a non-zero status."""
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        detail = lib.gptq_last_error().decode(errors="replace")
+        raise GPTQError(st, name, detail)
+
+
+def query(name: str, *args) -> int:
+    out = C.c_size_t(0)
+    call(name, *args, C.byref(out))
+    return int(out.value)

@@ -1,0 +1,201 @@
+// C ABI of the gfx950 GPTQ layer quantizer (declared in include/gptq.h).
+//
+// Every entry point validates all of its arguments on the host before it
+// touches HIP, so an error return means nothing was enqueued.  The library
+// allocates nothing; scratch space is the caller's workspace.
+#include <climits>
+#include <cstdio>
+#include <string>
+
+#include "../../include/gptq.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gptq_status fail(gptq_status st, const char* fn, const std::string& what) {
+  g_last_error = std::string(fn) + ": " + what;
+  return st;
+}
+
+gptq_status ok() {
+  g_last_error.clear();
+  return GPTQ_OK;
+}
+
+gptq_status check_launch(const char* fn) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GPTQ_EHIP, fn, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = 65535;       // H / U edge (grid y limit, int kernels)
+constexpr int64_t kMaxRows = INT_MAX / 2; // rows of W, tokens of X
+
+size_t elem_size(gptq_dtype t) { return t == GPTQ_F32 ? 4 : 2; }
+bool valid_dtype(int t) { return t == GPTQ_F32 || t == GPTQ_BF16 || t == GPTQ_F16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(gptq_status s) {
+  switch (s) {
+    case GPTQ_OK: return "GPTQ_OK";
+    case GPTQ_EINVAL: return "GPTQ_EINVAL: invalid argument";
+    case GPTQ_EDTYPE: return "GPTQ_EDTYPE: unsupported dtype";
+    case GPTQ_ESHAPE: return "GPTQ_ESHAPE: inconsistent shape or leading dimension";
+    case GPTQ_EALIGN: return "GPTQ_EALIGN: misaligned pointer or leading dimension";
+    case GPTQ_EUNSUPPORTED: return "GPTQ_EUNSUPPORTED: outside what this library supports";
+    case GPTQ_EWORKSPACE: return "GPTQ_EWORKSPACE: workspace missing or too small";
+    case GPTQ_EHIP: return "GPTQ_EHIP: HIP launch failed";
+  }
+  return "unknown gptq_status";
+}
+
+const char* gptq_last_error(void) { return g_last_error.c_str(); }
+
+// ------------------------------------------------------------------ Hessian
+gptq_status gptq_hessian_workspace_size(int64_t d, int64_t n_tok, gptq_dtype xt, size_t* bytes) {
+  const char* fn = "gptq_hessian_workspace_size";
+  if (!bytes) return fail(GPTQ_EINVAL, fn, "bytes is NULL");
+  if (d < 0 || n_tok < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (!valid_dtype(xt)) return fail(GPTQ_EDTYPE, fn, "xt must be GPTQ_F32, GPTQ_BF16 or GPTQ_F16");
+  if (d > kMaxDim || n_tok > kMaxRows) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  *bytes = 0;
+  if (xt != GPTQ_F32 && d > 0 && n_tok > 0) *bytes = gptq::syrk_workspace_bytes(gptq::plan_syrk(d, n_tok));
+  return ok();
+}
+
+gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, gptq_dtype xt, int64_t n_tok,
+                                    int64_t ldx, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "gptq_hessian_accumulate";
+  if (d < 0 || n_tok < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (!valid_dtype(xt)) return fail(GPTQ_EDTYPE, fn, "xt must be GPTQ_F32, GPTQ_BF16 or GPTQ_F16");
+  if (d > kMaxDim || n_tok > kMaxRows) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (d == 0 || n_tok == 0) return ok();
+  if (!H) return fail(GPTQ_EINVAL, fn, "H is NULL");
+  if (!X) return fail(GPTQ_EINVAL, fn, "X is NULL");
+  if (ldx < d) return fail(GPTQ_ESHAPE, fn, "ldx < d");
+  if (!aligned(H, 4)) return fail(GPTQ_EALIGN, fn, "H not 4-byte aligned");
+  if (xt == GPTQ_F32) {
+    if (!aligned(X, 4)) return fail(GPTQ_EALIGN, fn, "X not 4-byte aligned");
+  } else {
+    if (!aligned(X, 16) || (ldx % 8) != 0)
+      return fail(GPTQ_EALIGN, fn, "16-bit X needs a 16-byte aligned pointer and ldx % 8 == 0");
+  }
+  size_t need = 0;
+  if (xt != GPTQ_F32) need = gptq::syrk_workspace_bytes(gptq::plan_syrk(d, n_tok));
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(GPTQ_EWORKSPACE, fn, "workspace needs " + std::to_string(need) + " bytes");
+  if (need > 0 && !aligned(ws, 16)) return fail(GPTQ_EALIGN, fn, "workspace not 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (xt == GPTQ_F32) {
+    gptq::GemmArgs g;
+    g.M = (int)d; g.N = (int)d; g.K = (int)n_tok;
+    g.A = reinterpret_cast<const float*>(X); g.lda = ldx; g.a_trans = 1; g.a_mask = gptq::MASK_NONE; g.a_off = 0;
+    g.B = reinterpret_cast<const float*>(X); g.ldb = ldx; g.b_trans = 0; g.b_mask = gptq::MASK_NONE; g.b_off = 0;
+    g.C = H; g.ldc = d; g.alpha = 2.f; g.beta = 1.f; g.upper_only = 1;
+    gptq::launch_gemm_f32(g, s);
+  } else {
+    const gptq::SyrkPlan p = gptq::plan_syrk(d, n_tok);
+    gptq::launch_syrk16(H, d, X, xt == GPTQ_BF16 ? 1 : 2, n_tok, ldx, p, reinterpret_cast<float*>(ws), s);
+  }
+  return check_launch(fn);
+}
+
+// ------------------------------------------------------------------ prepare
+gptq_status gptq_prepare_workspace_size(int64_t d, int act_order, size_t* bytes) {
+  const char* fn = "gptq_prepare_workspace_size";
+  if (!bytes) return fail(GPTQ_EINVAL, fn, "bytes is NULL");
+  if (d < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (act_order != 0 && act_order != 1) return fail(GPTQ_EINVAL, fn, "act_order must be 0 or 1");
+  if (d > kMaxDim) return fail(GPTQ_EUNSUPPORTED, fn, "d too large");
+  *bytes = d > 0 ? gptq::prepare_workspace_bytes(d, act_order) : 0;
+  return ok();
+}
+
+gptq_status gptq_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t* perm,
+                         uint8_t* dead, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "gptq_prepare";
+  if (d < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (act_order != 0 && act_order != 1) return fail(GPTQ_EINVAL, fn, "act_order must be 0 or 1");
+  if (!(percdamp >= 0.f) || !(percdamp < 1e30f)) return fail(GPTQ_EINVAL, fn, "percdamp must be finite and >= 0");
+  if (d > kMaxDim) return fail(GPTQ_EUNSUPPORTED, fn, "d too large");
+  if (!info) return fail(GPTQ_EINVAL, fn, "info is NULL");
+  if (d == 0) return fail(GPTQ_EINVAL, fn, "d == 0 (nothing to factor)");
+  if (!H) return fail(GPTQ_EINVAL, fn, "H is NULL");
+  if (!dead) return fail(GPTQ_EINVAL, fn, "dead is NULL");
+  if (act_order && !perm) return fail(GPTQ_EINVAL, fn, "perm is NULL with act_order");
+  if (!aligned(H, 16) || !aligned(info, 4) || (perm && !aligned(perm, 4)))
+    return fail(GPTQ_EALIGN, fn, "H must be 16-byte aligned, perm and info 4-byte aligned");
+  const size_t need = gptq::prepare_workspace_bytes(d, act_order);
+  if (!ws || ws_bytes < need) return fail(GPTQ_EWORKSPACE, fn, "workspace needs " + std::to_string(need) + " bytes");
+  if (!aligned(ws, 256)) return fail(GPTQ_EALIGN, fn, "workspace not 256-byte aligned");
+  gptq::launch_prepare(H, d, percdamp, act_order, perm, dead, info, ws, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
+// ------------------------------------------------------------------ quantize
+gptq_status gptq_quantize_layer_workspace_size(int64_t r, int64_t c, int64_t blocksize, size_t* bytes) {
+  const char* fn = "gptq_quantize_layer_workspace_size";
+  if (!bytes) return fail(GPTQ_EINVAL, fn, "bytes is NULL");
+  if (r < 0 || c < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (blocksize < 1 || blocksize > 128) return fail(GPTQ_EUNSUPPORTED, fn, "blocksize must be 1..128");
+  if (r > kMaxRows || c > kMaxDim) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  *bytes = (r > 0 && c > 0) ? gptq::quantize_workspace_bytes(r, c, blocksize) : 0;
+  return ok();
+}
+
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t c, int64_t ldw,
+                                const float* U, const int32_t* perm, const uint8_t* dead, int bits,
+                                int64_t groupsize, int64_t blocksize, uint8_t* codes, float* scales,
+                                int32_t* zeros, int32_t* g_idx, float* W_hat, float* row_loss, void* ws,
+                                size_t ws_bytes, void* stream) {
+  const char* fn = "gptq_quantize_layer";
+  if (r < 0 || c < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (!valid_dtype(wt)) return fail(GPTQ_EDTYPE, fn, "wt must be GPTQ_F32, GPTQ_BF16 or GPTQ_F16");
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return fail(GPTQ_EUNSUPPORTED, fn, "bits must be 2, 3, 4 or 8");
+  if (blocksize < 1 || blocksize > 128) return fail(GPTQ_EUNSUPPORTED, fn, "blocksize must be 1..128");
+  if (groupsize > 0 && (groupsize % blocksize) != 0 && (blocksize % groupsize) != 0)
+    return fail(GPTQ_EUNSUPPORTED, fn, "groupsize must be a multiple or a divisor of blocksize");
+  if (r > kMaxRows || c > kMaxDim) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (r == 0 || c == 0) return ok();
+  if (ldw < c) return fail(GPTQ_ESHAPE, fn, "ldw < c");
+  if (!W || !U || !codes || !scales || !zeros || !g_idx) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
+  if (!aligned(W, elem_size(wt)) || !aligned(U, 4) || !aligned(scales, 4) || !aligned(zeros, 4) ||
+      !aligned(g_idx, 4) || (perm && !aligned(perm, 4)) || (W_hat && !aligned(W_hat, 4)) ||
+      (row_loss && !aligned(row_loss, 4)))
+    return fail(GPTQ_EALIGN, fn, "misaligned pointer");
+  const size_t need = gptq::quantize_workspace_bytes(r, c, blocksize);
+  if (!ws || ws_bytes < need) return fail(GPTQ_EWORKSPACE, fn, "workspace needs " + std::to_string(need) + " bytes");
+  if (!aligned(ws, 256)) return fail(GPTQ_EALIGN, fn, "workspace not 256-byte aligned");
+  gptq::QuantArgs a;
+  a.W = W; a.wt = (int)wt; a.r = r; a.c = c; a.ldw = ldw; a.U = U; a.perm = perm; a.dead = dead;
+  a.bits = bits; a.groupsize = groupsize; a.blocksize = blocksize; a.codes = codes; a.scales = scales;
+  a.zeros = zeros; a.g_idx = g_idx; a.W_hat = W_hat; a.row_loss = row_loss; a.ws = ws;
+  gptq::launch_quantize(a, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
+// ------------------------------------------------------------------ pack
+gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
+                      int64_t ld_words, void* stream) {
+  const char* fn = "gptq_pack";
+  if (r < 0 || c < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (bits != 3 && bits != 4) return fail(GPTQ_EUNSUPPORTED, fn, "packing supports 3 and 4 bits");
+  if (bits == 4 && c % 8 != 0) return fail(GPTQ_ESHAPE, fn, "4-bit packing needs c % 8 == 0");
+  if (bits == 3 && c % 32 != 0) return fail(GPTQ_ESHAPE, fn, "3-bit packing needs c % 32 == 0");
+  if (ld_words < c * bits / 32) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
+  if (r > kMaxRows || c > (int64_t)INT_MAX) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (r == 0 || c == 0) return ok();
+  if (!codes || !packed) return fail(GPTQ_EINVAL, fn, "codes or packed is NULL");
+  if (!aligned(codes, 16) || !aligned(packed, 4)) return fail(GPTQ_EALIGN, fn, "codes must be 16-byte aligned");
+  gptq::launch_pack(codes, r, c, bits, packed, ld_words, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
+}  // extern "C"

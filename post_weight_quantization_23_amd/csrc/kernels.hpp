@@ -1,0 +1,70 @@
+// Host-side launch interfaces of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gptq {
+
+enum { MASK_NONE = 0, MASK_UPPER = 1, MASK_LOWER = 2 };
+
+// See gemm_f32.hip for the exact contract.
+struct GemmArgs {
+  int M, N, K;
+  const float* A;
+  int64_t lda;
+  int a_trans, a_mask, a_off;
+  const float* B;
+  int64_t ldb;
+  int b_trans, b_mask, b_off;
+  float* C;
+  int64_t ldc;
+  float alpha, beta;
+  int upper_only;
+};
+void launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+
+// --- Hessian (syrk.hip) ---
+struct SyrkPlan {
+  int tile;        // output tile edge
+  int tiles;       // upper-triangle tiles
+  int splits;      // token splits (1 = accumulate straight into H)
+  int64_t chunk;   // tokens per split (multiple of the K-step)
+};
+SyrkPlan plan_syrk(int64_t d, int64_t n_tok);
+size_t syrk_workspace_bytes(const SyrkPlan& p);
+// dtype: 1 = bf16, 2 = fp16.  ws holds the split partials (may be null when
+// p.splits == 1).
+void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok, int64_t ldx,
+                   const SyrkPlan& p, float* ws, hipStream_t s);
+
+// --- Preparation (prepare.hip) ---
+size_t prepare_workspace_bytes(int64_t d, int act_order);
+void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t* perm,
+                    uint8_t* dead, int32_t* info, void* ws, hipStream_t s);
+
+// --- Quantization (quantize.hip) ---
+size_t quantize_workspace_bytes(int64_t r, int64_t c, int64_t blocksize);
+struct QuantArgs {
+  const void* W;
+  int wt;  // 0 f32, 1 bf16, 2 f16
+  int64_t r, c, ldw;
+  const float* U;
+  const int32_t* perm;
+  const uint8_t* dead;
+  int bits;
+  int64_t groupsize, blocksize;
+  uint8_t* codes;
+  float* scales;
+  int32_t* zeros;
+  int32_t* g_idx;
+  float* W_hat;
+  float* row_loss;
+  void* ws;
+};
+void launch_quantize(const QuantArgs& a, hipStream_t s);
+
+// --- Pack (pack.hip) ---
+void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
+                 int64_t ld_words, hipStream_t s);
+
+}  // namespace gptq

@@ -1,0 +1,78 @@
+// Packing of tick indices into 32-bit words (the pages store one tick index
+// per weight -- "GPTQ, with the code open", "What quantization is, and why
+// anyone bothers"; the word layout is this library's own):
+//   4 bits: 8 codes per word, code k of the word in bits 4k .. 4k+3;
+//   3 bits: 32 codes per 3 words, code k in bits 3k .. 3k+2 of the
+//           little-endian 96-bit value.
+// Streaming kernel: each thread turns one 8-byte (4-bit) or 32-byte (3-bit)
+// run of codes into one or three words.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gptq {
+
+namespace {
+
+__global__ __launch_bounds__(256) void pack4_kernel(const uint8_t* __restrict__ codes, int64_t r,
+                                                    int64_t c, uint32_t* __restrict__ out,
+                                                    int64_t ldw) {
+  const int64_t wpr = c / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= r * wpr) return;
+  const int64_t row = idx / wpr, wd = idx % wpr;
+  const uint2 v = *reinterpret_cast<const uint2*>(codes + row * c + wd * 8);
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    w |= ((v.x >> (8 * k)) & 0xFu) << (4 * k);
+    w |= ((v.y >> (8 * k)) & 0xFu) << (4 * (k + 4));
+  }
+  out[row * ldw + wd] = w;
+}
+
+__global__ __launch_bounds__(256) void pack3_kernel(const uint8_t* __restrict__ codes, int64_t r,
+                                                    int64_t c, uint32_t* __restrict__ out,
+                                                    int64_t ldw) {
+  const int64_t gpr = c / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= r * gpr) return;
+  const int64_t row = idx / gpr, grp = idx % gpr;
+  const u32x4* src = reinterpret_cast<const u32x4*>(codes + row * c + grp * 32);
+  const u32x4 a = src[0], b = src[1];
+  uint32_t byte4[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  uint64_t lo = 0, hi = 0;  // 96-bit accumulator: lo = bits 0..63, hi = bits 64..95
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint64_t v = (byte4[k >> 2] >> (8 * (k & 3))) & 0x7u;
+    const int sh = 3 * k;
+    if (sh + 3 <= 64) {
+      lo |= v << sh;
+    } else if (sh >= 64) {
+      hi |= v << (sh - 64);
+    } else {
+      lo |= v << sh;
+      hi |= v >> (64 - sh);
+    }
+  }
+  uint32_t* o = out + row * ldw + grp * 3;
+  o[0] = (uint32_t)lo;
+  o[1] = (uint32_t)(lo >> 32);
+  o[2] = (uint32_t)hi;
+}
+
+}  // namespace
+
+void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
+                 int64_t ld_words, hipStream_t s) {
+  if (bits == 4) {
+    const int64_t n = r * (c / 8);
+    hipLaunchKernelGGL(pack4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, r, c,
+                       packed, ld_words);
+  } else {
+    const int64_t n = r * (c / 32);
+    hipLaunchKernelGGL(pack3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, r, c,
+                       packed, ld_words);
+  }
+}
+
+}  // namespace gptq

@@ -1,0 +1,382 @@
+// GPTQ column loop on gfx950 ("GPTQ, with the code open", sections "What
+// quantization is, and why anyone bothers", "The repair rule", "From one
+// repair to a whole model" and "Paper vs. code").
+//
+// Per layer:
+//   init   : cast W to an fp32 working copy in processing order (columns
+//            gathered through perm, dead inputs zeroed); per-row rulers are
+//            fitted here, on the original weights, before that zeroing.
+//   blocks : for each block of B <= 128 columns
+//     chain  (block_kernel): for every row in parallel and the block's columns
+//            in order: quantize on the row's ruler, record the code, spread the
+//            error over the block's later columns with row j of U (the block's
+//            B x B corner of U staged in LDS), keep e = (w - w_hat) / U_jj;
+//     defer  (fp32 matrix-core GEMM): W[:, i2:] -= E * U[i1:i2, i2:].
+// Group rulers are fitted when the loop reaches a group's first column, on
+// the current values of its columns.
+//
+// Row mapping: L consecutive lanes own one row; lane p holds block columns
+// p, p + L, p + 2L, ... in registers, so column j belongs to lane j % L, slot
+// j / L.  The owner's scaled error e is broadcast to the row's other lanes
+// with one DPP move (quad_perm for L = 4, row_newbcast for L = 16).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gptq {
+
+namespace {
+
+constexpr int BMAX = 128;
+
+// Asymmetric min-max ruler ("What quantization is"): range stretched to
+// include 0, scale = (max - min) / (2^b - 1), zero = rne(-min / scale); an
+// all-zero range uses [-1, 1].  IEEE fp32 throughout.
+GPTQ_DEV void fit_ruler(float mn, float mx, float maxq, float& scale, float& zero) {
+  float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
+  if (lo == 0.f && hi == 0.f) {
+    lo = -1.f;
+    hi = 1.f;
+  }
+  scale = __fdiv_rn(hi - lo, maxq);
+  zero = rne(__fdiv_rn(-lo, scale));
+}
+
+// perm comes from device memory; an index outside [0, c) (a caller bug) is
+// clamped so that no access leaves the arrays.
+GPTQ_DEV int64_t clamp_col(int32_t v, int64_t c) { return v < 0 ? 0 : (v >= c ? c - 1 : (int64_t)v); }
+
+GPTQ_DEV float load_w(const void* W, int wt, int64_t idx) {
+  if (wt == 0) return reinterpret_cast<const float*>(W)[idx];
+  const uint16_t h = reinterpret_cast<const uint16_t*>(W)[idx];
+  if (wt == 1) return __uint_as_float((uint32_t)h << 16);
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// One workgroup per row: gather/cast into processing order, zero dead inputs,
+// per-row ruler on the original row.
+__global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp) {
+  const int64_t row = blockIdx.x;
+  const int64_t c = a.c;
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int64_t k = threadIdx.x; k < c; k += 256) {
+    const int64_t src = a.perm ? clamp_col(a.perm[k], c) : k;
+    const float v = load_w(a.W, a.wt, row * a.ldw + src);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+    const bool dk = a.dead && a.dead[src];
+    Wp[row * c + k] = dk ? 0.f : v;
+  }
+  if (a.groupsize <= 0) {
+    __shared__ float smn[256], smx[256];
+    smn[threadIdx.x] = mn;
+    smx[threadIdx.x] = mx;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) {
+        smn[threadIdx.x] = fminf(smn[threadIdx.x], smn[threadIdx.x + w]);
+        smx[threadIdx.x] = fmaxf(smx[threadIdx.x], smx[threadIdx.x + w]);
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      float scale, zero;
+      fit_ruler(smn[0], smx[0], (float)((1 << a.bits) - 1), scale, zero);
+      a.scales[row] = scale;
+      a.zeros[row] = (int32_t)zero;
+    }
+  }
+  if (threadIdx.x == 0 && a.row_loss) a.row_loss[row] = 0.f;
+}
+
+__global__ void gidx_kernel(const int32_t* perm, int64_t c, int64_t g, int32_t* g_idx) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= c) return;
+  const int64_t orig = perm ? clamp_col(perm[k], c) : k;
+  g_idx[orig] = g > 0 ? (int32_t)(k / g) : 0;
+}
+
+template <int L>
+GPTQ_DEV float bcast(float v, int src) {
+  const int iv = __float_as_int(v);
+  int r;
+  if constexpr (L == 4) {
+    switch (src) {
+      case 0: r = __builtin_amdgcn_mov_dpp(iv, 0x00, 0xF, 0xF, false); break;
+      case 1: r = __builtin_amdgcn_mov_dpp(iv, 0x55, 0xF, 0xF, false); break;
+      case 2: r = __builtin_amdgcn_mov_dpp(iv, 0xAA, 0xF, 0xF, false); break;
+      default: r = __builtin_amdgcn_mov_dpp(iv, 0xFF, 0xF, 0xF, false); break;
+    }
+  } else {
+    switch (src) {
+#define GPTQ_NB(n) \
+  case n: r = __builtin_amdgcn_update_dpp(0, iv, 0x150 + n, 0xF, 0xF, false); break;
+      GPTQ_NB(0) GPTQ_NB(1) GPTQ_NB(2) GPTQ_NB(3) GPTQ_NB(4) GPTQ_NB(5) GPTQ_NB(6) GPTQ_NB(7)
+      GPTQ_NB(8) GPTQ_NB(9) GPTQ_NB(10) GPTQ_NB(11) GPTQ_NB(12) GPTQ_NB(13) GPTQ_NB(14)
+      default: r = __builtin_amdgcn_update_dpp(0, iv, 0x150 + 15, 0xF, 0xF, false); break;
+#undef GPTQ_NB
+    }
+  }
+  return __int_as_float(r);
+}
+
+// Butterfly over the L lanes of a row (DPP within a 16-lane row).
+template <int L>
+GPTQ_DEV float row_min(float v) {
+  v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  if constexpr (L == 16) {
+    v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fminf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  }
+  return v;
+}
+template <int L>
+GPTQ_DEV float row_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  if constexpr (L == 16) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
+  }
+  return v;
+}
+template <int L>
+GPTQ_DEV float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if constexpr (L == 16) {
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  }
+  return v;
+}
+
+struct BlockArgs {
+  float* Wp;      // r x c working copy (processing order)
+  float* Et;      // Bw x r: scaled errors of this block, column-major per row
+  const float* U; // c x c
+  int64_t r, c, i1;
+  int Bw;
+  int bits;
+  int64_t groupsize;
+  const int32_t* perm;
+  uint8_t* codes;
+  float* scales;
+  int32_t* zeros;
+  float* W_hat;
+  float* row_loss;
+  int64_t n_groups;
+};
+
+// Fit the ruler of the group starting at block column j on the current
+// values of its columns (registers for the part inside the block, the working
+// copy for the part beyond it).
+template <int L, int S>
+GPTQ_DEV void fit_group(const float (&w)[S], int p, int j, int Bw, int64_t g, int64_t i1, int64_t c,
+                        const float* Wrow, bool valid, float maxq, float& scale, float& zero) {
+  const int64_t gend = min(i1 + j + g, c);
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    const int64_t col = i1 + p + L * m;
+    if (col >= i1 + j && col < gend && p + L * m < Bw) {
+      mn = fminf(mn, w[m]);
+      mx = fmaxf(mx, w[m]);
+    }
+  }
+  if (gend > i1 + Bw && valid) {
+    for (int64_t col = i1 + Bw + p; col < gend; col += L) {
+      const float v = Wrow[col];
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+  }
+  mn = row_min<L>(mn);
+  mx = row_max<L>(mx);
+  fit_ruler(mn, mx, maxq, scale, zero);
+}
+
+// MIDGROUPS: groups shorter than the block also start inside it.
+template <int L, bool MIDGROUPS>
+__global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
+  constexpr int S = BMAX / L;          // slots per lane
+  constexpr int ROWS = 256 / L;        // rows per workgroup
+  __shared__ __attribute__((aligned(16))) float Ul[BMAX * BMAX];  // Ul[j][p*S + m] = U[j][p + L m]
+  __shared__ float invd[BMAX];
+
+  const int tid = threadIdx.x;
+  const int p = tid % L;
+  const int64_t row = (int64_t)blockIdx.x * ROWS + tid / L;
+  const bool valid = row < a.r;
+  const int Bw = a.Bw;
+  const int64_t i1 = a.i1, c = a.c;
+  const float* Wrow = a.Wp + (valid ? row : 0) * c;
+
+  // Stage the block's corner of U: zero left of the diagonal and past Bw.
+  for (int e = tid; e < BMAX * BMAX; e += 256) {
+    const int j = e / BMAX, k = e % BMAX;
+    float v = 0.f;
+    if (j < Bw && k < Bw && k >= j) v = a.U[(i1 + j) * c + (i1 + k)];
+    Ul[j * BMAX + (k % L) * S + (k / L)] = v;
+  }
+  if (tid < BMAX) invd[tid] = tid < Bw ? __fdiv_rn(1.0f, a.U[(i1 + tid) * c + (i1 + tid)]) : 0.f;
+
+  float w[S];
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    const int col = p + L * m;
+    w[m] = (valid && col < Bw) ? Wrow[i1 + col] : 0.f;
+  }
+  __syncthreads();
+
+  const float maxq = (float)((1 << a.bits) - 1);
+  const int64_t g = a.groupsize;
+  float scale = 1.f, zero = 0.f;
+  if (g <= 0) {
+    if (valid) {
+      scale = a.scales[row * a.n_groups];
+      zero = (float)a.zeros[row * a.n_groups];
+    }
+  } else if (i1 % g == 0) {
+    fit_group<L, S>(w, p, 0, Bw, g, i1, c, Wrow, valid, maxq, scale, zero);
+    if (valid && p == 0) {
+      a.scales[row * a.n_groups + i1 / g] = scale;
+      a.zeros[row * a.n_groups + i1 / g] = (int32_t)zero;
+    }
+  }
+  float y = __fdiv_rn(1.0f, scale);
+  float qreg[S], whreg[S], ereg[S];
+#pragma unroll
+  for (int m = 0; m < S; ++m) qreg[m] = whreg[m] = ereg[m] = 0.f;
+  float loss = 0.f;
+  int next_group = MIDGROUPS ? (int)g : BMAX;
+
+#pragma unroll
+  for (int j = 0; j < BMAX; ++j) {
+    if (j >= Bw) break;
+    const int mj = j / L, pj = j % L;
+    if constexpr (MIDGROUPS) {
+      if (j > 0 && j == next_group) {
+        fit_group<L, S>(w, p, j, Bw, g, i1, c, Wrow, valid, maxq, scale, zero);
+        y = __fdiv_rn(1.0f, scale);
+        if (valid && p == 0) {
+          const int64_t gi = (i1 + j) / g;
+          a.scales[row * a.n_groups + gi] = scale;
+          a.zeros[row * a.n_groups + gi] = (int32_t)zero;
+        }
+        next_group += (int)g;
+      }
+    }
+    // Quantize column j (meaningful on the owner lane pj): the quotient is the
+    // correctly rounded x / scale (two FMA corrections of x * (1/scale)).
+    const float x = w[mj];
+    float t = div_by_recip(x, scale, y);
+    t = __builtin_fmaf(__builtin_fmaf(-t, scale, x), y, t);
+    const float q = fminf(fmaxf(rne(t) + zero, 0.f), maxq);
+    const float wh = __fmul_rn(scale, q - zero);
+    const float e = __fmul_rn(x - wh, invd[j]);
+    const bool own = (p == pj);
+    qreg[mj] = own ? q : qreg[mj];
+    whreg[mj] = own ? wh : whreg[mj];
+    ereg[mj] = own ? e : ereg[mj];
+    loss = own ? __builtin_fmaf(0.5f * e, e, loss) : loss;
+    // Repair every later column of the block: w_k -= e * U[j][k].
+    const float eb = bcast<L>(e, pj);
+    const float* urow = Ul + j * BMAX + p * S;
+#pragma unroll
+    for (int m = 0; m < S; ++m) {
+      if (m >= mj) w[m] = __builtin_fmaf(-eb, urow[m], w[m]);
+    }
+  }
+
+  loss = row_sum<L>(loss);
+  if (!valid) return;
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    const int col = p + L * m;
+    if (col < Bw) {
+      const int64_t pk = i1 + col;
+      const int64_t orig = a.perm ? clamp_col(a.perm[pk], c) : pk;
+      a.codes[row * c + orig] = (uint8_t)(int)qreg[m];
+      if (a.W_hat) a.W_hat[row * c + orig] = whreg[m];
+      a.Et[(int64_t)col * a.r + row] = ereg[m];
+    }
+  }
+  if (p == 0 && a.row_loss) a.row_loss[row] += loss;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int64_t r, int64_t c, int64_t blocksize) {
+  const int64_t B = blocksize > 0 ? blocksize : 1;
+  return align256((size_t)r * c * sizeof(float)) + align256((size_t)B * r * sizeof(float));
+}
+
+void launch_quantize(const QuantArgs& a, hipStream_t s) {
+  const int64_t r = a.r, c = a.c;
+  float* Wp = reinterpret_cast<float*>(a.ws);
+  float* Et = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + align256((size_t)r * c * sizeof(float)));
+  hipLaunchKernelGGL(init_kernel, dim3((unsigned)r), dim3(256), 0, s, a, Wp);
+  hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, s, a.perm, c,
+                     a.groupsize, a.g_idx);
+  BlockArgs b;
+  b.Wp = Wp;
+  b.Et = Et;
+  b.U = a.U;
+  b.r = r;
+  b.c = c;
+  b.bits = a.bits;
+  b.groupsize = a.groupsize;
+  b.perm = a.perm;
+  b.codes = a.codes;
+  b.scales = a.scales;
+  b.zeros = a.zeros;
+  b.W_hat = a.W_hat;
+  b.row_loss = a.row_loss;
+  b.n_groups = a.groupsize > 0 ? (c + a.groupsize - 1) / a.groupsize : 1;
+  const int64_t B = a.blocksize;
+  // 16 lanes per row when there are enough rows to fill the chip that way.
+  const bool wide = r * 16 >= 256 * 64;
+  for (int64_t i1 = 0; i1 < c; i1 += B) {
+    const int Bw = (int)std::min<int64_t>(B, c - i1);
+    b.i1 = i1;
+    b.Bw = Bw;
+    const bool mid = a.groupsize > 0 && a.groupsize < B;
+    const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
+    if (wide && mid)
+      hipLaunchKernelGGL((block_kernel<16, true>), g16, dim3(256), 0, s, b);
+    else if (wide)
+      hipLaunchKernelGGL((block_kernel<16, false>), g16, dim3(256), 0, s, b);
+    else if (mid)
+      hipLaunchKernelGGL((block_kernel<4, true>), g4, dim3(256), 0, s, b);
+    else
+      hipLaunchKernelGGL((block_kernel<4, false>), g4, dim3(256), 0, s, b);
+    const int64_t i2 = i1 + Bw;
+    if (i2 < c) {
+      GemmArgs gm;
+      gm.M = (int)r;
+      gm.N = (int)(c - i2);
+      gm.K = Bw;
+      gm.A = Et;
+      gm.lda = r;
+      gm.a_trans = 1;
+      gm.a_mask = MASK_NONE;
+      gm.a_off = 0;
+      gm.B = a.U + i1 * c + i2;
+      gm.ldb = c;
+      gm.b_trans = 0;
+      gm.b_mask = MASK_NONE;
+      gm.b_off = 0;
+      gm.C = Wp + i2;
+      gm.ldc = c;
+      gm.alpha = -1.f;
+      gm.beta = 1.f;
+      gm.upper_only = 0;
+      launch_gemm_f32(gm, s);
+    }
+  }
+}
+
+}  // namespace gptq

@@ -1,0 +1,167 @@
+"""Python binding of the gfx950 GPTQ layer quantizer (argument marshalling only).
+
+The names follow the C ABI in include/gptq.h; every step runs in the HIP
+library.  Tensors must live on the current HIP device; work is enqueued on
+torch's current stream.  Method: the GPTQ layer quantizer of "GPTQ, with the
+code open" (sections "Measuring damage where it matters", "The repair rule",
+"From one repair to a whole model", "Paper vs. code").
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib
+from ._lib import GPTQ_BF16, GPTQ_F16, GPTQ_F32, GPTQError
+
+__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "Workspace",
+           "NotPositiveDefinite", "GPTQError"]
+
+_DT = {torch.float32: GPTQ_F32, torch.bfloat16: GPTQ_BF16, torch.float16: GPTQ_F16}
+
+
+class NotPositiveDefinite(RuntimeError):
+    """The damped Hessian has no Cholesky factor (info > 0) or holds NaN/Inf (info < 0)."""
+
+
+def _ptr(t):
+    return C.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, ndim=None, dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+class Workspace:
+    """A reusable device scratch buffer (grown on demand, 256-byte aligned)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        return self.buf, self.buf.numel()
+
+
+def _ws(ws, nbytes, device):
+    if ws is None:
+        ws = Workspace()
+    return ws.get(nbytes, device)
+
+
+def hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ws: Workspace | None = None) -> None:
+    """H[i][j] += 2 sum_t X[t][i] X[t][j] on the upper triangle (H fp32 [d, d], X [N, d])."""
+    _need(H, "H", torch.float32, 2)
+    _need(X, "X", None, 2, H.device)
+    if X.dtype not in _DT:
+        raise TypeError("X must be float32, bfloat16 or float16")
+    d = H.shape[0]
+    if H.shape != (d, d) or not H.is_contiguous():
+        raise ValueError("H must be a contiguous square matrix")
+    if X.shape[1] != d or X.stride(1) != 1:
+        raise ValueError("X must be [tokens, d] with unit feature stride")
+    n = X.shape[0]
+    xt = _DT[X.dtype]
+    need = _lib.query("gptq_hessian_workspace_size", d, n, xt)
+    buf, nb = _ws(ws, need, H.device)
+    _lib.call("gptq_hessian_accumulate", _ptr(H), d, _ptr(X), xt, n, X.stride(0), _ptr(buf), nb, _stream())
+
+
+def prepare(H: torch.Tensor, percdamp: float = 0.01, act_order: bool = False, check: bool = True,
+            ws: Workspace | None = None):
+    """Replace H (fp32 [d, d], upper triangle) by U = chol_upper(H_damped^{-1}) in place.
+
+    Returns (perm int32 [d], dead uint8 [d], info int32 [1]).  With check=True the
+    call synchronises and raises NotPositiveDefinite when info != 0.
+    """
+    _need(H, "H", torch.float32, 2)
+    d = H.shape[0]
+    if H.shape != (d, d) or not H.is_contiguous():
+        raise ValueError("H must be a contiguous square matrix")
+    perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    dead = torch.empty(d, dtype=torch.uint8, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    need = _lib.query("gptq_prepare_workspace_size", d, int(act_order))
+    buf, nb = _ws(ws, need, H.device)
+    _lib.call("gptq_prepare", _ptr(H), d, float(percdamp), int(act_order), _ptr(perm), _ptr(dead), _ptr(info),
+              _ptr(buf), nb, _stream())
+    if check:
+        v = int(info.item())
+        if v != 0:
+            raise NotPositiveDefinite(f"gptq_prepare info = {v}")
+    return perm, dead, info
+
+
+def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor | None, dead: torch.Tensor | None,
+                   bits: int = 4, groupsize: int = 128, blocksize: int = 128, want_w_hat: bool = False,
+                   want_loss: bool = True, ws: Workspace | None = None, out: dict | None = None) -> dict:
+    """GPTQ-quantize W [r, c] with the factor U from prepare().
+
+    Returns {codes uint8 [r, c], scales fp32 [r, G], zeros int32 [r, G], g_idx int32 [c],
+    w_hat fp32 [r, c] or None, row_loss fp32 [r] or None}; outputs are in the
+    original column order.  `out` may supply preallocated tensors with those keys.
+    """
+    _need(W, "W", None, 2)
+    if W.dtype not in _DT:
+        raise TypeError("W must be float32, bfloat16 or float16")
+    if W.stride(1) != 1:
+        raise ValueError("W must have unit column stride")
+    r, c = W.shape
+    _need(U, "U", torch.float32, 2, W.device)
+    if U.shape != (c, c) or not U.is_contiguous():
+        raise ValueError("U must be a contiguous [c, c] matrix")
+    if perm is not None:
+        _need(perm, "perm", torch.int32, 1, W.device)
+    if dead is not None:
+        _need(dead, "dead", torch.uint8, 1, W.device)
+    G = (c + groupsize - 1) // groupsize if groupsize > 0 else 1
+    dev = W.device
+    o = dict(out or {})
+    codes = o.get("codes") if o.get("codes") is not None else torch.empty((r, c), dtype=torch.uint8, device=dev)
+    scales = o.get("scales") if o.get("scales") is not None else torch.empty((r, G), dtype=torch.float32, device=dev)
+    zeros = o.get("zeros") if o.get("zeros") is not None else torch.empty((r, G), dtype=torch.int32, device=dev)
+    g_idx = o.get("g_idx") if o.get("g_idx") is not None else torch.empty(c, dtype=torch.int32, device=dev)
+    w_hat = o.get("w_hat")
+    if want_w_hat and w_hat is None:
+        w_hat = torch.empty((r, c), dtype=torch.float32, device=dev)
+    row_loss = o.get("row_loss")
+    if want_loss and row_loss is None:
+        row_loss = torch.empty(r, dtype=torch.float32, device=dev)
+    need = _lib.query("gptq_quantize_layer_workspace_size", r, c, blocksize)
+    buf, nb = _ws(ws, need, dev)
+    _lib.call("gptq_quantize_layer", _ptr(W), _DT[W.dtype], r, c, W.stride(0), _ptr(U), _ptr(perm), _ptr(dead),
+              int(bits), int(groupsize), int(blocksize), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+              _ptr(w_hat), _ptr(row_loss), _ptr(buf), nb, _stream())
+    return {"codes": codes, "scales": scales, "zeros": zeros, "g_idx": g_idx, "w_hat": w_hat,
+            "row_loss": row_loss}
+
+
+def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Pack uint8 codes [r, c] into uint32 words [r, c*bits/32] (layout in include/gptq.h)."""
+    _need(codes, "codes", torch.uint8, 2)
+    if not codes.is_contiguous():
+        raise ValueError("codes must be contiguous")
+    r, c = codes.shape
+    nw = c * bits // 32
+    if out is None:
+        out = torch.empty((r, nw), dtype=torch.uint32, device=codes.device)
+    _lib.call("gptq_pack", _ptr(codes), r, c, int(bits), _ptr(out), out.stride(0), _stream())
+    return out
