@@ -71,8 +71,9 @@ typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
  * X      : n_tok x d calibration inputs, token-major (one row per token),
  *          row stride ldx >= d elements, dtype xt (GPTQ_BF16, GPTQ_F16 or
  *          GPTQ_F32).  Products are formed exactly and summed in fp32.
- *          bf16/fp16 X needs a 16-byte aligned pointer and ldx % 8 == 0
- *          (GPTQ_EALIGN otherwise).  n_tok == 0 or d == 0 is a no-op.
+ *          X must be aligned to its element size (GPTQ_EALIGN otherwise);
+ *          16-bit X that is 16-byte aligned with ldx % 8 == 0 takes the fast
+ *          load path.  n_tok == 0 or d == 0 is a no-op.
  * ws     : workspace of at least gptq_hessian_workspace_size() bytes
  *          (may be NULL when that size is 0); 256-byte aligned.
  * ------------------------------------------------------------------------ */

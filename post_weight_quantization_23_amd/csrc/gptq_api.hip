@@ -84,8 +84,7 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, gptq_dty
   if (xt == GPTQ_F32) {
     if (!aligned(X, 4)) return fail(GPTQ_EALIGN, fn, "X not 4-byte aligned");
   } else {
-    if (!aligned(X, 16) || (ldx % 8) != 0)
-      return fail(GPTQ_EALIGN, fn, "16-bit X needs a 16-byte aligned pointer and ldx % 8 == 0");
+    if (!aligned(X, 2)) return fail(GPTQ_EALIGN, fn, "16-bit X not 2-byte aligned");
   }
   size_t need = 0;
   if (xt != GPTQ_F32) need = gptq::syrk_workspace_bytes(gptq::plan_syrk(d, n_tok));

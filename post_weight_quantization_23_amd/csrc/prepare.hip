@@ -127,40 +127,61 @@ __global__ __launch_bounds__(256) void zero_lower_kernel(float* H, int64_t d) {
 // triangle of the (updated) H block; it is replaced by U = V^{-1} where
 // V V^T = block, V upper.  One backward sweep j = 31 .. 0 does both:
 //   factor : V[:, j] = A[:, j] / sqrt(A[j][j]);  A[0:j, 0:j] -= V[0:j, j] V[0:j, j]^T
-//   invert : X[j, :] /= V[j][j];  X[0:j, j:] -= V[0:j, j] X[j, j:]   (X starts as I)
+//   invert : X[j, :] /= V[j][j];  X[0:j, :] -= V[0:j, j] X[j, :]   (X starts as I)
 // (row j of X is final at step j: every later row has already been removed).
-// X lives in `X32` (32 x 33).  A non-positive or NaN pivot sets *info once.
-__device__ void leaf32(float* M, int o, float* X32, int32_t* info, int64_t gbase, int pad) {
+// Lane (k, h) = (lane & 31, lane >> 5) keeps column k of A and of X for the
+// rows i = 2m + h in registers.  Each step publishes the scaled column j of V
+// (zero from row j down) and row j of X through LDS (`cbuf`, 64 floats), so
+// both rank-1 updates are unconditional: entries they must not touch get a
+// zero factor.  A non-positive or NaN pivot sets *info once.
+__device__ __forceinline__ void leaf32(float* M, int o, float* cbuf, int32_t* info, int64_t gbase, int pad) {
   const int lane = threadIdx.x & 63;
-  const int col = lane & 31, half = lane >> 5;
-  for (int e = lane; e < 32 * 32; e += 64) X32[(e >> 5) * 33 + (e & 31)] = ((e >> 5) == (e & 31)) ? 1.f : 0.f;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+  const int k = lane & 31, h = lane >> 5;
+  float a[16], x[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    a[m] = M[(o + 2 * m + h) * LDM + o + k];
+    x[m] = (2 * m + h == k) ? 1.f : 0.f;
+  }
+#pragma unroll
   for (int j = 31; j >= 0; --j) {
-    const float piv = M[(o + j) * LDM + o + j];
+    const int jm = j >> 1, jh = j & 1;
+    // pivot A[j][j]: row j = 2*jm + jh of column j, held by lane j + 32*jh
+    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jm]), j + 32 * jh));
     if (lane == 0 && !(piv > 0.f) && (o + j) >= pad) {
       if (*info == 0) *info = (int32_t)(gbase + (o + j - pad) + 1);
     }
-    const float v = __fsqrt_rn(piv);
-    const float rv = __fdiv_rn(1.0f, v);
-    if (lane < j) M[(o + lane) * LDM + o + j] *= rv;
-    if (lane >= 32 && col >= j) X32[j * 33 + col] *= rv;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (col < j) {
-      const float vk = M[(o + col) * LDM + o + j];
-      for (int i = half; i <= col; i += 2)
-        M[(o + i) * LDM + o + col] -= M[(o + i) * LDM + o + j] * vk;
-    } else {
-      const float xj = X32[j * 33 + col];
-      for (int r = half; r < j; r += 2) X32[r * 33 + col] -= M[(o + r) * LDM + o + j] * xj;
+    const float rv = __fdiv_rn(1.0f, __fsqrt_rn(piv));
+    // column j of V (rows < j) and row j of X, published through LDS
+    if (k == j) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) cbuf[2 * m + h] = (2 * m + h < j) ? a[m] * rv : 0.f;
+    }
+    if (h == jh) {
+      x[jm] *= rv;
+      cbuf[32 + k] = x[jm];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float vk = cbuf[k];
+    const float xj = cbuf[32 + k];
+    float vi[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) vi[m] = cbuf[2 * m + h];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      a[m] = __builtin_fmaf(-vi[m], vk, a[m]);
+      x[m] = __builtin_fmaf(-vi[m], xj, x[m]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  for (int e = lane; e < 32 * 32; e += 64) {
-    const int i = e >> 5, k = e & 31;
-    M[(o + i) * LDM + o + k] = (k >= i) ? X32[i * 33 + k] : 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int i = 2 * m + h;
+    M[(o + i) * LDM + o + k] = (k >= i) ? x[m] : 0.f;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -170,7 +191,7 @@ __device__ void leaf32(float* M, int o, float* X32, int32_t* info, int64_t gbase
 // cores; n, m, K multiples of 32.  op(B) = B^T (B stored m x K) when bt, else
 // B (K x m).  32 x 32 output blocks are spread over the 4 waves; with
 // upper_only, blocks strictly below the diagonal are skipped.
-__device__ void lds_gemm(int n, int m, int K, const float* A, int lda, const float* B, int ldb, int bt,
+__device__ __forceinline__ void lds_gemm(int n, int m, int K, const float* A, int lda, const float* B, int ldb, int bt,
                          float* C, int ldc, float alpha, bool accumulate, bool upper_only) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nbm = m / 32, blocks = (n / 32) * nbm;
@@ -181,6 +202,7 @@ __device__ void lds_gemm(int n, int m, int K, const float* A, int lda, const flo
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
     const int r = 32 * bi + (lane & 31), c = 32 * bj + (lane & 31), kh = lane >> 5;
+#pragma unroll 8
     for (int k = 0; k < K; k += 2) {
       const float a = A[r * lda + k + kh];
       const float b = bt ? B[c * ldb + k + kh] : B[(k + kh) * ldb + c];
@@ -204,9 +226,9 @@ struct LeafScratch {
 };
 
 template <int N>
-__device__ void leaf_rec(float* M, int o, const LeafScratch& ts, int32_t* info, int64_t gbase, int pad) {
+__device__ __forceinline__ void leaf_rec(float* M, int o, const LeafScratch& ts, int32_t* info, int64_t gbase, int pad) {
   if constexpr (N == 32) {
-    if ((threadIdx.x >> 6) == 0) leaf32(M, o, ts.X32, info, gbase, pad);
+    if ((threadIdx.x >> 6) == 0) leaf32(M, o, ts.X32, info, gbase, pad);  // X32: 64-float exchange buffer
     __syncthreads();
   } else {
     constexpr int h = N / 2;
@@ -318,7 +340,7 @@ void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t*
                     int32_t* info, void* ws, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)leaf_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)leaf_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)leaf_smem_bytes());
     attr_set = true;
   }

@@ -12,6 +12,12 @@
 //            error over the block's later columns with row j of U (the block's
 //            B x B corner of U staged in LDS), keep e = (w - w_hat) / U_jj;
 //     defer  (fp32 matrix-core GEMM): W[:, i2:] -= E * U[i1:i2, i2:].
+//   The deferral is two-level: inside a super-block of 4 blocks the product
+//   for the rest of the super-block follows each block, and the product for
+//   every later column follows the super-block (K = 4B).  Every column still
+//   receives every repair before its own turn, so the values are those of the
+//   plain loop up to rounding order, while the trailing columns are read and
+//   written 4x less often.
 // Group rulers are fitted when the loop reaches a group's first column, on
 // the current values of its columns.
 //
@@ -196,8 +202,10 @@ GPTQ_DEV void fit_group(const float (&w)[S], int p, int j, int Bw, int64_t g, in
   fit_ruler(mn, mx, maxq, scale, zero);
 }
 
-// MIDGROUPS: groups shorter than the block also start inside it.
-template <int L, bool MIDGROUPS>
+// MIDGROUPS: groups shorter than the block also start inside it.  FULL: the
+// block has all BMAX columns (no per-step bound check, so the compiler can
+// schedule LDS reads of later steps early).
+template <int L, bool MIDGROUPS, bool FULL>
 __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   constexpr int S = BMAX / L;          // slots per lane
   constexpr int ROWS = 256 / L;        // rows per workgroup
@@ -208,7 +216,7 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   const int p = tid % L;
   const int64_t row = (int64_t)blockIdx.x * ROWS + tid / L;
   const bool valid = row < a.r;
-  const int Bw = a.Bw;
+  const int Bw = FULL ? BMAX : a.Bw;
   const int64_t i1 = a.i1, c = a.c;
   const float* Wrow = a.Wp + (valid ? row : 0) * c;
 
@@ -243,6 +251,11 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
       a.scales[row * a.n_groups + i1 / g] = scale;
       a.zeros[row * a.n_groups + i1 / g] = (int32_t)zero;
     }
+  } else if (valid) {
+    // A group longer than the block continues here: its ruler was fitted (and
+    // stored) by the block holding the group's first column.
+    scale = a.scales[row * a.n_groups + i1 / g];
+    zero = (float)a.zeros[row * a.n_groups + i1 / g];
   }
   float y = __fdiv_rn(1.0f, scale);
   float qreg[S], whreg[S], ereg[S];
@@ -251,9 +264,9 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   float loss = 0.f;
   int next_group = MIDGROUPS ? (int)g : BMAX;
 
-#pragma unroll
+#pragma clang loop unroll(full)
   for (int j = 0; j < BMAX; ++j) {
-    if (j >= Bw) break;
+    if (!FULL && j >= Bw) continue;
     const int mj = j / L, pj = j % L;
     if constexpr (MIDGROUPS) {
       if (j > 0 && j == next_group) {
@@ -309,10 +322,51 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
+constexpr int64_t SUPER_BLOCKS = 4;
+
 size_t quantize_workspace_bytes(int64_t r, int64_t c, int64_t blocksize) {
   const int64_t B = blocksize > 0 ? blocksize : 1;
-  return align256((size_t)r * c * sizeof(float)) + align256((size_t)B * r * sizeof(float));
+  return align256((size_t)r * c * sizeof(float)) + align256((size_t)SUPER_BLOCKS * B * r * sizeof(float));
 }
+
+namespace {
+
+// Columns whose repairs are applied at once before the deferred product:
+// SUPER_BLOCKS blocks when that keeps every group inside one super-block or
+// starting at a super-block start (so a group's ruler always sees fully
+// repaired values), else one block.
+int64_t super_block(int64_t B, int64_t g) {
+  const int64_t sb = SUPER_BLOCKS * B;
+  if (g <= 0 || sb % g == 0 || g % sb == 0) return sb;
+  return B;
+}
+
+void gemm_update(hipStream_t s, int64_t r, int64_t c, const float* Et, int K, const float* U, int64_t k0,
+                 int64_t n0, int64_t n1, float* Wp) {
+  // Wp[:, n0:n1] -= E * U[k0:k0+K, n0:n1], E stored K x r (row k = column k of E)
+  GemmArgs gm;
+  gm.M = (int)r;
+  gm.N = (int)(n1 - n0);
+  gm.K = K;
+  gm.A = Et;
+  gm.lda = r;
+  gm.a_trans = 1;
+  gm.a_mask = MASK_NONE;
+  gm.a_off = 0;
+  gm.B = U + k0 * c + n0;
+  gm.ldb = c;
+  gm.b_trans = 0;
+  gm.b_mask = MASK_NONE;
+  gm.b_off = 0;
+  gm.C = Wp + n0;
+  gm.ldc = c;
+  gm.alpha = -1.f;
+  gm.beta = 1.f;
+  gm.upper_only = 0;
+  launch_gemm_f32(gm, s);
+}
+
+}  // namespace
 
 void launch_quantize(const QuantArgs& a, hipStream_t s) {
   const int64_t r = a.r, c = a.c;
@@ -323,7 +377,6 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
                      a.groupsize, a.g_idx);
   BlockArgs b;
   b.Wp = Wp;
-  b.Et = Et;
   b.U = a.U;
   b.r = r;
   b.c = c;
@@ -337,45 +390,34 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   b.row_loss = a.row_loss;
   b.n_groups = a.groupsize > 0 ? (c + a.groupsize - 1) / a.groupsize : 1;
   const int64_t B = a.blocksize;
+  const int64_t SB = super_block(B, a.groupsize);
   // 16 lanes per row when there are enough rows to fill the chip that way.
   const bool wide = r * 16 >= 256 * 64;
-  for (int64_t i1 = 0; i1 < c; i1 += B) {
-    const int Bw = (int)std::min<int64_t>(B, c - i1);
-    b.i1 = i1;
-    b.Bw = Bw;
-    const bool mid = a.groupsize > 0 && a.groupsize < B;
-    const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
-    if (wide && mid)
-      hipLaunchKernelGGL((block_kernel<16, true>), g16, dim3(256), 0, s, b);
-    else if (wide)
-      hipLaunchKernelGGL((block_kernel<16, false>), g16, dim3(256), 0, s, b);
-    else if (mid)
-      hipLaunchKernelGGL((block_kernel<4, true>), g4, dim3(256), 0, s, b);
-    else
-      hipLaunchKernelGGL((block_kernel<4, false>), g4, dim3(256), 0, s, b);
-    const int64_t i2 = i1 + Bw;
-    if (i2 < c) {
-      GemmArgs gm;
-      gm.M = (int)r;
-      gm.N = (int)(c - i2);
-      gm.K = Bw;
-      gm.A = Et;
-      gm.lda = r;
-      gm.a_trans = 1;
-      gm.a_mask = MASK_NONE;
-      gm.a_off = 0;
-      gm.B = a.U + i1 * c + i2;
-      gm.ldb = c;
-      gm.b_trans = 0;
-      gm.b_mask = MASK_NONE;
-      gm.b_off = 0;
-      gm.C = Wp + i2;
-      gm.ldc = c;
-      gm.alpha = -1.f;
-      gm.beta = 1.f;
-      gm.upper_only = 0;
-      launch_gemm_f32(gm, s);
+  const bool mid = a.groupsize > 0 && a.groupsize < B;
+  const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
+  for (int64_t s1 = 0; s1 < c; s1 += SB) {
+    const int64_t s2 = std::min(s1 + SB, c);
+    for (int64_t i1 = s1; i1 < s2; i1 += B) {
+      const int Bw = (int)std::min<int64_t>(B, s2 - i1);
+      const int64_t i2 = i1 + Bw;
+      b.i1 = i1;
+      b.Bw = Bw;
+      b.Et = Et + (i1 - s1) * r;
+      const bool full = Bw == BMAX;
+#define GPTQ_BLOCK(LL, MID, FU, G) hipLaunchKernelGGL((block_kernel<LL, MID, FU>), G, dim3(256), 0, s, b)
+      if (wide) {
+        if (mid) { if (full) GPTQ_BLOCK(16, true, true, g16); else GPTQ_BLOCK(16, true, false, g16); }
+        else     { if (full) GPTQ_BLOCK(16, false, true, g16); else GPTQ_BLOCK(16, false, false, g16); }
+      } else {
+        if (mid) { if (full) GPTQ_BLOCK(4, true, true, g4); else GPTQ_BLOCK(4, true, false, g4); }
+        else     { if (full) GPTQ_BLOCK(4, false, true, g4); else GPTQ_BLOCK(4, false, false, g4); }
+      }
+#undef GPTQ_BLOCK
+      // repairs of this block's errors to the rest of the super-block, at once
+      if (i2 < s2) gemm_update(s, r, c, b.Et, Bw, a.U, i1, i2, s2, Wp);
     }
+    // repairs of the whole super-block to every later column, deferred to here
+    if (s2 < c) gemm_update(s, r, c, Et, (int)(s2 - s1), a.U, s1, s2, c, Wp);
   }
 }
 

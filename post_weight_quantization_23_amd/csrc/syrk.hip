@@ -7,12 +7,14 @@
 // fp32 and the sums are fp32 (v_mfma_f32_32x32x16_{bf16,f16}).
 //
 // Work split: 256 x 256 output tiles of the upper triangle, times `splits`
-// contiguous token ranges.  Each workgroup (4 waves, each a 128 x 128 quarter
-// of the tile as 4 x 4 MFMA blocks) streams its token range in K-steps of 64.
+// contiguous token ranges.  Each workgroup (8 waves, each a 128 x 64 block of
+// the tile as 4 x 2 MFMA blocks) streams its token range in K-steps of 64.
 // A K-step of X arrives feature-contiguous; each thread loads an 8-token x
 // 8-feature patch (eight 16-byte loads), transposes it in registers with
 // v_perm_b32, and writes eight 16-byte token-contiguous rows into LDS, so
-// every MFMA operand is a single 16-byte LDS read.  LDS rows are 128 bytes
+// every MFMA operand is a single 16-byte LDS read.  The loads run two K-steps
+// ahead and the transposes of the next step are interleaved with the first
+// MFMAs of the current one.  LDS rows are 128 bytes
 // (64 tokens) with the 16-byte chunks XOR-swizzled by the row index, which
 // keeps both the transposed writes and the MFMA reads free of bank conflicts.
 // With one split the tile is added straight into H; otherwise partial tiles
@@ -32,18 +34,54 @@ constexpr int ROWB = KSTEP * 2;  // bytes per LDS row (64 x 16-bit)
 
 GPTQ_DEV int swz(int f) { return (f ^ (f >> 3)) & 7; }
 
+constexpr int NXCD = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int SUPER = 4;  // tiles per super-tile edge in the compact tile order
+
+// The t-th upper-triangle tile (bi <= bj) in super-tile order: super-tiles of
+// SUPER x SUPER tiles are visited row by row over the upper triangle, and the
+// tiles inside each one row by row, so consecutive t share row/column slabs.
 GPTQ_DEV void tile_coords(int t, int nt, int& bi, int& bj) {
-  int rem = t;
-  bi = 0;
-  while (rem >= nt - bi) {
-    rem -= nt - bi;
-    ++bi;
+  const int ns = (nt + SUPER - 1) / SUPER;
+  for (int si = 0; si < ns; ++si) {
+    for (int sj = si; sj < ns; ++sj) {
+      const int r0 = si * SUPER, r1 = min(nt, r0 + SUPER);
+      const int c0 = sj * SUPER, c1 = min(nt, c0 + SUPER);
+      int cnt = 0;
+      for (int r = r0; r < r1; ++r) cnt += max(0, c1 - max(c0, r));
+      if (t < cnt) {
+        for (int r = r0; r < r1; ++r) {
+          const int n = max(0, c1 - max(c0, r));
+          if (t < n) {
+            bi = r;
+            bj = max(c0, r) + t;
+            return;
+          }
+          t -= n;
+        }
+      }
+      t -= cnt;
+    }
   }
-  bj = bi + rem;
+  bi = bj = 0;  // not reached for t < tiles
+}
+
+// Workgroup w runs on XCD w % NXCD.  Give each XCD one contiguous run of the
+// (split-major, compact tile order) work list, so the workgroups one XCD runs
+// at the same time read the same token range of the same feature slabs and
+// share them in that XCD's L2.  Returns false for padding workgroups.
+GPTQ_DEV bool work_unit(int w, int tiles, int splits, int per_xcd, int& tile, int& split) {
+  const int v = (w % NXCD) * per_xcd + w / NXCD;
+  if (w / NXCD >= per_xcd || v >= tiles * splits) return false;
+  split = v / tiles;
+  tile = v % tiles;
+  return true;
 }
 
 // Load the 8 x 8 patch (tokens t0..t0+7, features f0..f0+7) as eight rows of
-// 4 dwords (two 16-bit features each).  Out-of-range entries are zero.
+// 4 dwords (two 16-bit features each).  Out-of-range entries are zero.  VEC:
+// X is 16-byte aligned with ldx % 8 == 0, so a full row of the patch is one
+// 16-byte load; otherwise 16-bit loads.
+template <bool VEC>
 GPTQ_DEV void load_patch(const uint16_t* X, int64_t ldx, int64_t t0, int64_t t_end, int f0, int d,
                          u32x4 v[8]) {
   const bool full_f = f0 + 8 <= d;
@@ -53,7 +91,7 @@ GPTQ_DEV void load_patch(const uint16_t* X, int64_t ldx, int64_t t0, int64_t t_e
     u32x4 r = {0u, 0u, 0u, 0u};
     if (t < t_end) {
       const uint16_t* p = X + t * ldx + f0;
-      if (full_f) {
+      if (VEC && full_f) {
         r = *reinterpret_cast<const u32x4*>(p);
       } else {
         uint32_t h[8];
@@ -64,26 +102,6 @@ GPTQ_DEV void load_patch(const uint16_t* X, int64_t ldx, int64_t t0, int64_t t_e
       }
     }
     v[i] = r;
-  }
-}
-
-// Transpose the patch: o[m] holds feature m for tokens 0..7 (two per dword).
-GPTQ_DEV void transpose_patch(const u32x4 v[8], u32x4 o[8]) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      o[m][u] = __builtin_amdgcn_perm(v[2 * u + 1][m >> 1], v[2 * u][m >> 1], sel);
-  }
-}
-
-GPTQ_DEV void store_patch(unsigned char* lds, int fb, int tb, const u32x4 o[8]) {
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int f = fb * 8 + m;
-    const int chunk = tb ^ swz(f);
-    *reinterpret_cast<u32x4*>(lds + f * ROWB + chunk * 16) = o[m];
   }
 }
 
@@ -98,80 +116,118 @@ GPTQ_DEV floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c) {
   }
 }
 
-template <int DT>
-__global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+template <int DT, bool VEC>
+__global__ __launch_bounds__(512, 1) void syrk16_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                          int64_t n_tok, int d, int nt,
                                                          int64_t chunk, float* __restrict__ H,
                                                          float* __restrict__ part, int tiles,
-                                                         int splits, int* __restrict__ counters) {
+                                                         int splits, int* __restrict__ counters,
+                                                         int per_xcd) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // LDS: A buffers 0/1 then B buffers 0/1, TILE rows of ROWB bytes each.
   auto a_buf = [&](int b) { return smem + b * (TILE * ROWB); };
   auto b_buf = [&](int b) { return smem + (2 + b) * (TILE * ROWB); };
 
+  int tile, split;
+  if (!work_unit(blockIdx.x, tiles, splits, per_xcd, tile, split)) return;
   int bi, bj;
-  tile_coords(blockIdx.x, nt, bi, bj);
+  tile_coords(tile, nt, bi, bj);
   const bool diag = bi == bj;
   const int fi0 = bi * TILE, fj0 = bj * TILE;
-  const int64_t t_beg = (int64_t)blockIdx.y * chunk;
+  const int64_t t_beg = (int64_t)split * chunk;
   const int64_t t_end = min(n_tok, t_beg + chunk);
 
+  // 8 waves as 2 (rows) x 4 (columns) of 128 x 64 output blocks.
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
-  const int tb = tid >> 5, fb = tid & 31;
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+  // Loader role: threads 0..255 carry patches of the row slab (A), threads
+  // 256..511 patches of the column slab (B, not needed on diagonal tiles).
+  const bool is_b = tid >= 256;
+  const int ptid = tid & 255;
+  const int tb = ptid >> 5, fb = ptid & 31;
+  const int f_slab = is_b ? fj0 : fi0;
+  const bool loads = !(is_b && diag);
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  u32x4 va[8], vb[8], o[8];
-  auto fetch = [&](int64_t t0) {
-    load_patch(X, ldx, t0 + tb * 8, t_end, fi0 + fb * 8, d, va);
-    if (!diag) load_patch(X, ldx, t0 + tb * 8, t_end, fj0 + fb * 8, d, vb);
-  };
-  auto stage = [&](int buf) {
-    transpose_patch(va, o);
-    store_patch(a_buf(buf), fb, tb, o);
-    if (!diag) {
-      transpose_patch(vb, o);
-      store_patch(b_buf(buf), fb, tb, o);
+  // Software pipeline over K-steps of 64 tokens with one register set: at the
+  // start of step s the registers hold the raw patch of step s+1.  During the
+  // first half of step s's MFMAs (LDS buffer s&1) that patch is transposed
+  // into the other LDS buffer; the loads of step s+2 are then issued into the
+  // freed registers and have the rest of step s and the start of step s+1 to
+  // arrive.
+  u32x4 rg[8];
+  const bool inside = VEC && (fi0 + TILE <= d) && (fj0 + TILE <= d);
+  const int64_t nsteps = (t_end - t_beg + KSTEP - 1) / KSTEP;
+
+  auto fetch = [&](int64_t st) {
+    if (!loads) return;
+    const int64_t t0 = t_beg + st * KSTEP + tb * 8;
+    if (inside && t_beg + (st + 1) * KSTEP <= t_end) {
+      const uint16_t* pa = X + t0 * ldx + f_slab + fb * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rg[i] = *reinterpret_cast<const u32x4*>(pa + i * ldx);
+    } else {
+      load_patch<VEC>(X, ldx, t0, t_end, f_slab + fb * 8, d, rg);
     }
   };
+  // Transpose rows m0 .. m0+3 of the patch and write them to LDS.
+  auto stage4 = [&](int buf, int m0) {
+    if (!loads) return;
+    unsigned char* lds = is_b ? b_buf(buf) : a_buf(buf);
+#pragma unroll
+    for (int m = m0; m < m0 + 4; ++m) {
+      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+      u32x4 o;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = __builtin_amdgcn_perm(rg[2 * u + 1][m >> 1], rg[2 * u][m >> 1], sel);
+      const int f = fb * 8 + m;
+      *reinterpret_cast<u32x4*>(lds + f * ROWB + ((tb ^ swz(f)) * 16)) = o;
+    }
+  };
+  auto mfma_kk = [&](const unsigned char* as, const unsigned char* bs, int kk) {
+    const int chunk_id = 2 * kk + (lane >> 5);
+    u32x4 a[4], b[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = wm + 32 * i + (lane & 31);
+      a[i] = *reinterpret_cast<const u32x4*>(as + f * ROWB + ((chunk_id ^ swz(f)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int f = wn + 32 * j + (lane & 31);
+      b[j] = *reinterpret_cast<const u32x4*>(bs + f * ROWB + ((chunk_id ^ swz(f)) * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<DT>(a[i], b[j], acc[i][j]);
+  };
 
-  if (t_beg < t_end) {
-    fetch(t_beg);
-    stage(0);
+  if (nsteps > 0) {
+    fetch(0);
+    stage4(0, 0);
+    stage4(0, 4);
+    if (nsteps > 1) fetch(1);
     __syncthreads();
     int buf = 0;
-    for (int64_t t0 = t_beg; t0 < t_end; t0 += KSTEP) {
-      const bool more = t0 + KSTEP < t_end;
-      if (more) fetch(t0 + KSTEP);
+    for (int64_t st = 0; st < nsteps; ++st) {
+      const bool stage_next = st + 1 < nsteps;
       const unsigned char* as = a_buf(buf);
       const unsigned char* bs = diag ? a_buf(buf) : b_buf(buf);
-#pragma unroll
-      for (int kk = 0; kk < KSTEP / 16; ++kk) {
-        const int chunk_id = 2 * kk + (lane >> 5);
-        u32x4 a[4], b[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int f = wm + 32 * i + (lane & 31);
-          a[i] = *reinterpret_cast<const u32x4*>(as + f * ROWB + ((chunk_id ^ swz(f)) * 16));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int f = wn + 32 * j + (lane & 31);
-          b[j] = *reinterpret_cast<const u32x4*>(bs + f * ROWB + ((chunk_id ^ swz(f)) * 16));
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<DT>(a[i], b[j], acc[i][j]);
-      }
-      if (more) stage(buf ^ 1);
+      mfma_kk(as, bs, 0);
+      if (stage_next) stage4(buf ^ 1, 0);
+      mfma_kk(as, bs, 1);
+      if (stage_next) stage4(buf ^ 1, 4);
+      if (st + 2 < nsteps) fetch(st + 2);
+      mfma_kk(as, bs, 2);
+      mfma_kk(as, bs, 3);
       __syncthreads();
       buf ^= 1;
     }
@@ -182,7 +238,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int gj = fj0 + wn + 32 * j + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -194,11 +250,11 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
         }
       }
   } else {
-    float* pt = part + ((int64_t)blockIdx.y * tiles + blockIdx.x) * (TILE * TILE);
+    float* pt = part + ((int64_t)split * tiles + tile) * (TILE * TILE);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int c = wn + 32 * j + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -211,12 +267,12 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
     __shared__ int last;
     __threadfence();
     __syncthreads();
-    if (tid == 0) last = (atomicAdd(&counters[blockIdx.x], 1) == splits - 1);
+    if (tid == 0) last = (atomicAdd(&counters[tile], 1) == splits - 1);
     __syncthreads();
     if (!last) return;
     __threadfence();
-    const float* p0 = part + (int64_t)blockIdx.x * (TILE * TILE);
-    for (int e4 = tid; e4 < TILE * TILE / 4; e4 += 256) {
+    const float* p0 = part + (int64_t)tile * (TILE * TILE);
+    for (int e4 = tid; e4 < TILE * TILE / 4; e4 += 512) {
       const int r = e4 / (TILE / 4), c = (e4 % (TILE / 4)) * 4;
       floatx4 sum = {0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < splits; ++k)
@@ -230,7 +286,7 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
           if (gj + q < d) hp[q] = __builtin_fmaf(2.0f, sum[q], hp[q]);
       }
     }
-    if (tid == 0) counters[blockIdx.x] = 0;
+    if (tid == 0) counters[tile] = 0;
   }
 }
 
@@ -280,23 +336,32 @@ void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok,
   const size_t shmem = 4 * TILE * ROWB;  // 128 KiB: A and B, double buffered
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute((const void*)syrk16_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    hipFuncSetAttribute((const void*)syrk16_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    (void)hipFuncSetAttribute((const void*)syrk16_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    (void)hipFuncSetAttribute((const void*)syrk16_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     attr_set = true;
   }
-  dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
+  const int units = p.tiles * p.splits;
+  const int per_xcd = (units + NXCD - 1) / NXCD;
+  dim3 grid((unsigned)(per_xcd * NXCD));
   float* part = p.splits > 1 ? ws : nullptr;
   int* counters = nullptr;
   if (p.splits > 1) {
     counters = reinterpret_cast<int*>(ws + (size_t)p.splits * p.tiles * TILE * TILE);
     hipLaunchKernelGGL(zero_counters_kernel, dim3((p.tiles + 255) / 256), dim3(256), 0, s, counters, p.tiles);
   }
-  if (dtype == 1)
-    hipLaunchKernelGGL(syrk16_kernel<1>, grid, dim3(256), shmem, s, (const uint16_t*)X, ldx, n_tok,
-                       (int)d, nt, p.chunk, H, part, p.tiles, p.splits, counters);
-  else
-    hipLaunchKernelGGL(syrk16_kernel<2>, grid, dim3(256), shmem, s, (const uint16_t*)X, ldx, n_tok,
-                       (int)d, nt, p.chunk, H, part, p.tiles, p.splits, counters);
+  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
+  const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
+#define GPTQ_SYRK_LAUNCH(DT, V)                                                                        \
+  hipLaunchKernelGGL((syrk16_kernel<DT, V>), grid, dim3(512), shmem, s, Xh, ldx, n_tok, (int)d, nt, \
+                     p.chunk, H, part, p.tiles, p.splits, counters, per_xcd)
+  if (dtype == 1) {
+    if (vec) GPTQ_SYRK_LAUNCH(1, true); else GPTQ_SYRK_LAUNCH(1, false);
+  } else {
+    if (vec) GPTQ_SYRK_LAUNCH(2, true); else GPTQ_SYRK_LAUNCH(2, false);
+  }
+#undef GPTQ_SYRK_LAUNCH
 }
 
 }  // namespace gptq

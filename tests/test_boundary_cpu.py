@@ -72,8 +72,8 @@ def test_hessian_argument_errors(lib):
     assert _st(lib, f, ALIGNED, 8, None, 1, 4, 8, None, 0, None) == 1      # X NULL
     assert _st(lib, f, ALIGNED, 8, ALIGNED, 7, 4, 8, None, 0, None) == 2   # dtype
     assert _st(lib, f, ALIGNED, 8, ALIGNED, 1, 4, 4, None, 0, None) == 3   # ldx < d
-    assert _st(lib, f, ALIGNED, 8, C.c_void_p(0x10002), 1, 4, 8, None, 0, None) == 4  # X misaligned
-    assert _st(lib, f, ALIGNED, 8, ALIGNED, 1, 4, 12, None, 0, None) == 4  # ldx % 8
+    assert _st(lib, f, ALIGNED, 8, C.c_void_p(0x10001), 1, 4, 8, None, 0, None) == 4  # X misaligned
+    assert _st(lib, f, ALIGNED, 8, C.c_void_p(0x10002), 0, 4, 8, None, 0, None) == 4  # fp32 X misaligned
     # bf16 at a size that needs split partials: workspace required
     assert _st(lib, f, ALIGNED, 4096, ALIGNED, 1, 262144, 4096, None, 0, None) == 6
     assert "workspace" in lib.gptq_last_error().decode()

@@ -44,10 +44,10 @@ def to_dev(a, dtype):
 DT = {"float32": torch.float32, "bfloat16": torch.bfloat16, "float16": torch.float16}
 
 
-def gpu_hessian(X_host, xdtype, batches=1):
+def gpu_hessian(X_host, xdtype, batches=1, pad=0):
     d = X_host.shape[1]
     H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
-    X = to_dev(X_host, DT[xdtype])
+    X = to_dev(np.pad(X_host, ((0, 0), (0, pad))), DT[xdtype])[:, :d]   # row stride d + pad
     for part in torch.tensor_split(X, batches, dim=0):
         gq().hessian_accumulate(H, part)
     torch.cuda.synchronize()
@@ -121,15 +121,17 @@ def test_pack_matches_oracle(bits, r, c):
 
 
 # -------------------------------------------------------------------- Hessian
-@pytest.mark.parametrize("xdtype,n,d,batches", [
-    ("float32", 2048, 256, 1),      # the small fp32 workload
-    ("bfloat16", 2048 + 37, 256, 1),
-    ("float16", 1000, 300, 2),      # ragged tile and ragged tokens, two batches
-    ("bfloat16", 4096, 520, 3),
+@pytest.mark.parametrize("xdtype,n,d,batches,pad", [
+    ("float32", 2048, 256, 1, 0),      # the small fp32 workload
+    ("bfloat16", 2048 + 37, 256, 1, 0),
+    ("float16", 1000, 300, 2, 0),      # ragged tile, ragged tokens, unaligned rows, two batches
+    ("bfloat16", 4096, 520, 3, 8),     # strided rows (ldx = d + 8)
+    ("float32", 777, 130, 2, 3),
+    ("bfloat16", 70000, 512, 1, 0),    # split over tokens: partial tiles summed in the kernel
 ])
-def test_hessian_matches_oracle(xdtype, n, d, batches):
+def test_hessian_matches_oracle(xdtype, n, d, batches, pad):
     X = S.activations_host(n, d, "t4", outliers=4, gain=20.0, wid=50 + d, dtype=xdtype)
-    H = gpu_hessian(X, xdtype, batches)
+    H = gpu_hessian(X, xdtype, batches, pad)
     check_h(H, ref.hessian(X))
 
 
@@ -180,6 +182,8 @@ CASES = [
     (1100, 256, 4, 128, 128, False, 0, "bfloat16"),  # 16 lanes per row path
     (1024, 320, 3, 32, 64, True, 1, "bfloat16"),     # 16 lanes, groups inside blocks
     (20, 300, 4, 256, 128, False, 0, "float32"),     # group spanning two blocks
+    (1030, 1100, 4, 128, 128, True, 2, "bfloat16"),  # several super-blocks, ragged tail
+    (70, 1300, 3, 256, 64, False, 0, "float16"),     # groups of 4 blocks across super-blocks
 ]
 
 
@@ -256,4 +260,4 @@ def test_empty_inputs_are_no_ops():
     assert float(H.abs().sum()) == 0.0
     out = q.quantize_layer(torch.zeros((0, 64), device="cuda"), torch.eye(64, device="cuda"), None, None)
     assert out["codes"].shape == (0, 64)
-    assert q.pack(torch.zeros((0, 64), dtype=torch.uint8, device="cuda"), 4).shape == (0, 32)
+    assert q.pack(torch.zeros((0, 64), dtype=torch.uint8, device="cuda"), 4).shape == (0, 8)
