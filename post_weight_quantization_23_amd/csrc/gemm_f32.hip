@@ -14,8 +14,8 @@
 // SYRK-shaped update; M == N).  beta == 0 never reads C.
 //
 // Tiling: TM x TN output tile per 256-thread workgroup, 2 x 2 waves, each
-// wave (TM/2) x (TN/2) as 32x32 MFMA blocks; K-step 32 staged through LDS in
-// k-major rows (As[k][m], Bs[k][n]) with double buffering.
+// wave (TM/2) x (TN/2) as 32x32 MFMA blocks; K-steps of KT staged through LDS
+// in k-major rows (As[k][m], Bs[k][n]) with double buffering.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -23,15 +23,7 @@ namespace gptq {
 
 namespace {
 
-constexpr int KT = 32;
 constexpr int PAD = 4;
-
-template <int TM>
-struct TileLoader {
-  // Loads the logical TM x KT tile op(X)[row0 .. row0+TM, k0 .. k0+KT) into
-  // registers (16 floats per thread for TM = 128, 8 for TM = 64).
-  static constexpr int NV = TM * KT / 4 / 256;  // float4 per thread
-};
 
 GPTQ_DEV bool keep_a(int mask, int off, int m, int k) {
   // A logical [m][k]
@@ -64,13 +56,15 @@ GPTQ_DEV floatx4 load4(const float* base, int64_t ld, int row, int col, int rows
   return v;
 }
 
-template <int TM, int TN>
+template <int TM, int TN, int KT>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   constexpr int WM = TM / 2, WN = TN / 2;   // per-wave tile
   constexpr int MB = WM / 32, NB = WN / 32; // 32x32 blocks per wave
   constexpr int LDA_S = TM + PAD, LDB_S = TN + PAD;
-  __shared__ __attribute__((aligned(16))) float As[2][KT * LDA_S];
-  __shared__ __attribute__((aligned(16))) float Bs[2][KT * LDB_S];
+  extern __shared__ __attribute__((aligned(16))) float gemm_smem[];
+  // LDS: A buffers 0/1 (KT x LDA_S each), then B buffers 0/1 (KT x LDB_S).
+  auto As = [&](int b) { return gemm_smem + b * (KT * LDA_S); };
+  auto Bs = [&](int b) { return gemm_smem + 2 * (KT * LDA_S) + b * (KT * LDB_S); };
 
   const int tiles_n = (g.N + TN - 1) / TN;
   const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
@@ -157,10 +151,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       if (!g.a_trans) {
         int m = idx / (KT / 4), k4 = idx % (KT / 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) As[buf][(4 * k4 + c) * LDA_S + m] = ra[u][c];
+        for (int c = 0; c < 4; ++c) As(buf)[(4 * k4 + c) * LDA_S + m] = ra[u][c];
       } else {
         int k = idx / (TM / 4), m4 = idx % (TM / 4);
-        *reinterpret_cast<floatx4*>(&As[buf][k * LDA_S + 4 * m4]) = ra[u];
+        *reinterpret_cast<floatx4*>(As(buf) + k * LDA_S + 4 * m4) = ra[u];
       }
     }
 #pragma unroll
@@ -168,11 +162,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       int idx = tid + 256 * u;
       if (!g.b_trans) {
         int k = idx / (TN / 4), n4 = idx % (TN / 4);
-        *reinterpret_cast<floatx4*>(&Bs[buf][k * LDB_S + 4 * n4]) = rb[u];
+        *reinterpret_cast<floatx4*>(Bs(buf) + k * LDB_S + 4 * n4) = rb[u];
       } else {
         int n = idx / (KT / 4), k4 = idx % (KT / 4);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) Bs[buf][(4 * k4 + c) * LDB_S + n] = rb[u][c];
+        for (int c = 0; c < 4; ++c) Bs(buf)[(4 * k4 + c) * LDB_S + n] = rb[u][c];
       }
     }
   };
@@ -185,8 +179,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     for (int k0 = k_lo; k0 < k_hi; k0 += KT) {
       const bool more = k0 + KT < k_hi;
       if (more) load_tile(k0 + KT);
-      const float* as = As[buf];
-      const float* bs = Bs[buf];
+      const float* as = As(buf);
+      const float* bs = Bs(buf);
 #pragma unroll
       for (int kk = 0; kk < KT / 2; ++kk) {
         const int kr = 2 * kk + (lane >> 5);
@@ -226,18 +220,29 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     }
 }
 
+template <int TM, int TN, int KT>
+void launch_tile(const GemmArgs& g, hipStream_t s) {
+  constexpr size_t smem = (size_t)2 * KT * ((TM + PAD) + (TN + PAD)) * sizeof(float);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)gemm_f32_kernel<TM, TN, KT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)smem);
+    attr = true;
+  }
+  const int64_t tiles = (int64_t)((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
+  hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, KT>), dim3((unsigned)tiles), dim3(256), smem, s, g);
+}
+
 }  // namespace
 
+// Tile choice: 128 x 128 when that already gives enough workgroups, else 64 x 64.
 void launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return;
   const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
   if (t128 >= 480) {
-    dim3 grid((unsigned)t128);
-    hipLaunchKernelGGL((gemm_f32_kernel<128, 128>), grid, dim3(256), 0, s, g);
+    launch_tile<128, 128, 32>(g, s);
   } else {
-    const int64_t t64 = (int64_t)((g.M + 63) / 64) * ((g.N + 63) / 64);
-    dim3 grid((unsigned)t64);
-    hipLaunchKernelGGL((gemm_f32_kernel<64, 64>), grid, dim3(256), 0, s, g);
+    launch_tile<64, 64, 32>(g, s);
   }
 }
 

@@ -129,59 +129,41 @@ __global__ __launch_bounds__(256) void zero_lower_kernel(float* H, int64_t d) {
 //   factor : V[:, j] = A[:, j] / sqrt(A[j][j]);  A[0:j, 0:j] -= V[0:j, j] V[0:j, j]^T
 //   invert : X[j, :] /= V[j][j];  X[0:j, :] -= V[0:j, j] X[j, :]   (X starts as I)
 // (row j of X is final at step j: every later row has already been removed).
-// Lane (k, h) = (lane & 31, lane >> 5) keeps column k of A and of X for the
-// rows i = 2m + h in registers.  Each step publishes the scaled column j of V
-// (zero from row j down) and row j of X through LDS (`cbuf`, 64 floats), so
-// both rank-1 updates are unconditional: entries they must not touch get a
-// zero factor.  A non-positive or NaN pivot sets *info once.
-__device__ __forceinline__ void leaf32(float* M, int o, float* cbuf, int32_t* info, int64_t gbase, int pad) {
+// Registers only: lane k < 32 holds column k of the symmetric block A, lane
+// 32 + c column c of X.  With p = A[j][j] and a_i = A[i][j] (read from lane j),
+// both updates are  col[i] -= a_i * col[j] / p  for i < j  -- on the A side
+// col[j] = A[j][k] = A[k][j] by symmetry, on the X side col[j] = X[j][c] before
+// its scaling -- and the X side then scales col[j] by 1/sqrt(p).  A non-positive
+// or NaN pivot sets *info once.
+__device__ __forceinline__ void leaf32(float* M, int o, float* /*unused*/, int32_t* info, int64_t gbase,
+                                       int pad) {
   const int lane = threadIdx.x & 63;
-  const int k = lane & 31, h = lane >> 5;
-  float a[16], x[16];
+  const int k = lane & 31;
+  const bool xside = lane >= 32;
+  float col[32];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    a[m] = M[(o + 2 * m + h) * LDM + o + k];
-    x[m] = (2 * m + h == k) ? 1.f : 0.f;
+  for (int i = 0; i < 32; ++i) {
+    const float av = M[(o + min(i, k)) * LDM + o + max(i, k)];
+    col[i] = xside ? (i == k ? 1.f : 0.f) : av;
   }
 #pragma unroll
   for (int j = 31; j >= 0; --j) {
-    const int jm = j >> 1, jh = j & 1;
-    // pivot A[j][j]: row j = 2*jm + jh of column j, held by lane j + 32*jh
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[jm]), j + 32 * jh));
+    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(col[j]), j));
     if (lane == 0 && !(piv > 0.f) && (o + j) >= pad) {
       if (*info == 0) *info = (int32_t)(gbase + (o + j - pad) + 1);
     }
-    const float rv = __fdiv_rn(1.0f, __fsqrt_rn(piv));
-    // column j of V (rows < j) and row j of X, published through LDS
-    if (k == j) {
+    const float rv = __builtin_amdgcn_rsqf(piv);   // 1/sqrt(pivot), ~1 ulp
+    const float f = col[j] * (rv * rv);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) cbuf[2 * m + h] = (2 * m + h < j) ? a[m] * rv : 0.f;
+    for (int i = 0; i < j; ++i) {
+      const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(col[i]), j));
+      col[i] = __builtin_fmaf(-ai, f, col[i]);
     }
-    if (h == jh) {
-      x[jm] *= rv;
-      cbuf[32 + k] = x[jm];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const float vk = cbuf[k];
-    const float xj = cbuf[32 + k];
-    float vi[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) vi[m] = cbuf[2 * m + h];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      a[m] = __builtin_fmaf(-vi[m], vk, a[m]);
-      x[m] = __builtin_fmaf(-vi[m], xj, x[m]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (xside) col[j] *= rv;
   }
+  if (xside) {
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    const int i = 2 * m + h;
-    M[(o + i) * LDM + o + k] = (k >= i) ? x[m] : 0.f;
+    for (int i = 0; i < 32; ++i) M[(o + i) * LDM + o + k] = (k >= i) ? col[i] : 0.f;
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -265,23 +247,52 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* H, int64_t d, int64_t 
   ts.T32b = ts.T32a + 32 * 33;
   ts.X32 = ts.T32b + 32 * 33;
   const int pad = NB - n;
-  for (int e = threadIdx.x; e < NB * NB; e += 256) {
-    const int i = e / NB, k = e % NB;
-    float v;
-    if (i < pad || k < pad) {
-      v = (i == k) ? 1.f : 0.f;
-    } else if (k >= i) {
-      v = H[(o + i - pad) * d + (o + k - pad)];
-    } else {
-      v = 0.f;
+  const bool fast = pad == 0 && (d % 4) == 0 && (o % 4) == 0;
+  if (fast) {
+    // 16 float4 per thread, all issued before any is used: element group
+    // e = tid + 256 u is row e / 32, columns 4 (e % 32) .. +3.
+    floatx4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = threadIdx.x + 256 * u, i = e >> 5, k4 = (e & 31) * 4;
+      v[u] = *reinterpret_cast<const floatx4*>(H + (o + i) * d + o + k4);
     }
-    M[i * LDM + k] = v;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = threadIdx.x + 256 * u, i = e >> 5, k4 = (e & 31) * 4;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) M[i * LDM + k4 + c] = (k4 + c >= i) ? v[u][c] : 0.f;
+    }
+  } else {
+    for (int e = threadIdx.x; e < NB * NB; e += 256) {
+      const int i = e / NB, k = e % NB;
+      float v;
+      if (i < pad || k < pad) {
+        v = (i == k) ? 1.f : 0.f;
+      } else if (k >= i) {
+        v = H[(o + i - pad) * d + (o + k - pad)];
+      } else {
+        v = 0.f;
+      }
+      M[i * LDM + k] = v;
+    }
   }
   __syncthreads();
   leaf_rec<NB>(M, 0, ts, info, o, pad);
-  for (int e = threadIdx.x; e < n * n; e += 256) {
-    const int i = e / n, k = e % n;
-    H[(o + i) * d + (o + k)] = (k >= i) ? M[(i + pad) * LDM + (k + pad)] : 0.f;
+  if (fast) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = threadIdx.x + 256 * u, i = e >> 5, k4 = (e & 31) * 4;
+      floatx4 w;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = (k4 + c >= i) ? M[i * LDM + k4 + c] : 0.f;
+      *reinterpret_cast<floatx4*>(H + (o + i) * d + o + k4) = w;
+    }
+  } else {
+    for (int e = threadIdx.x; e < n * n; e += 256) {
+      const int i = e / n, k = e % n;
+      H[(o + i) * d + (o + k)] = (k >= i) ? M[(i + pad) * LDM + (k + pad)] : 0.f;
+    }
   }
 }
 

@@ -209,7 +209,8 @@ template <int L, bool MIDGROUPS, bool FULL>
 __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   constexpr int S = BMAX / L;          // slots per lane
   constexpr int ROWS = 256 / L;        // rows per workgroup
-  __shared__ __attribute__((aligned(16))) float Ul[BMAX * BMAX];  // Ul[j][p*S + m] = U[j][p + L m]
+  constexpr int SP = S, URS = BMAX;  // Ul[j][p*S + m] = U[j][p + L m]
+  __shared__ __attribute__((aligned(16))) float Ul[BMAX * URS];
   __shared__ float invd[BMAX];
 
   const int tid = threadIdx.x;
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
     const int j = e / BMAX, k = e % BMAX;
     float v = 0.f;
     if (j < Bw && k < Bw && k >= j) v = a.U[(i1 + j) * c + (i1 + k)];
-    Ul[j * BMAX + (k % L) * S + (k / L)] = v;
+    Ul[j * URS + (k % L) * SP + (k / L)] = v;
   }
   if (tid < BMAX) invd[tid] = tid < Bw ? __fdiv_rn(1.0f, a.U[(i1 + tid) * c + (i1 + tid)]) : 0.f;
 
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
     loss = own ? __builtin_fmaf(0.5f * e, e, loss) : loss;
     // Repair every later column of the block: w_k -= e * U[j][k].
     const float eb = bcast<L>(e, pj);
-    const float* urow = Ul + j * BMAX + p * S;
+    const float* urow = Ul + j * URS + p * SP;
 #pragma unroll
     for (int m = 0; m < S; ++m) {
       if (m >= mj) w[m] = __builtin_fmaf(-eb, urow[m], w[m]);
