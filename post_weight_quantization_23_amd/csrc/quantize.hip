@@ -9,8 +9,9 @@
 //   blocks : for each block of B <= 128 columns
 //     chain  (block_kernel): for every row in parallel and the block's columns
 //            in order: quantize on the row's ruler, record the code, spread the
-//            error over the block's later columns with row j of U (the block's
-//            B x B corner of U staged in LDS), keep e = (w - w_hat) / U_jj;
+//            error err = w - w_hat over the block's later columns with row j of
+//            V = U / U_jj (the block's B x B corner, staged in LDS), keep the
+//            scaled error e = err / U_jj;
 //     defer  (fp32 matrix-core GEMM): W[:, i2:] -= E * U[i1:i2, i2:].
 //   The deferral is two-level: inside a super-block of 4 blocks the product
 //   for the rest of the super-block follows each block, and the product for
@@ -23,8 +24,12 @@
 //
 // Row mapping: L consecutive lanes own one row; lane p holds block columns
 // p, p + L, p + 2L, ... in registers, so column j belongs to lane j % L, slot
-// j / L.  The owner's scaled error e is broadcast to the row's other lanes
-// with one DPP move (quad_perm for L = 4, row_newbcast for L = 16).
+// j / L.  The owner's error is broadcast to the row's other lanes with one DPP
+// move (quad_perm for L = 4, row_newbcast for L = 16).  The per-column
+// dependency chain is thereby five instructions: multiply by 1/scale, round,
+// clamp, one FMA for the error, the broadcast (plus the FMA repairing the next
+// column); codes, errors and the check of the fast decisions are recomputed
+// once per block from the values the columns had at their turn.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -115,10 +120,10 @@ GPTQ_DEV float bcast(float v, int src) {
   } else {
     switch (src) {
 #define GPTQ_NB(n) \
-  case n: r = __builtin_amdgcn_update_dpp(0, iv, 0x150 + n, 0xF, 0xF, false); break;
+  case n: r = __builtin_amdgcn_mov_dpp(iv, 0x150 + n, 0xF, 0xF, true); break;
       GPTQ_NB(0) GPTQ_NB(1) GPTQ_NB(2) GPTQ_NB(3) GPTQ_NB(4) GPTQ_NB(5) GPTQ_NB(6) GPTQ_NB(7)
       GPTQ_NB(8) GPTQ_NB(9) GPTQ_NB(10) GPTQ_NB(11) GPTQ_NB(12) GPTQ_NB(13) GPTQ_NB(14)
-      default: r = __builtin_amdgcn_update_dpp(0, iv, 0x150 + 15, 0xF, 0xF, false); break;
+      default: r = __builtin_amdgcn_mov_dpp(iv, 0x150 + 15, 0xF, 0xF, true); break;
 #undef GPTQ_NB
     }
   }
@@ -159,7 +164,8 @@ GPTQ_DEV float row_sum(float v) {
 
 struct BlockArgs {
   float* Wp;      // r x c working copy (processing order)
-  float* Et;      // Bw x r: scaled errors of this block, column-major per row
+  float* E;       // scaled errors of this block: E[row * lde + k], k = 0 .. Bw - 1
+  int64_t lde;
   const float* U; // c x c
   int64_t r, c, i1;
   int Bw;
@@ -172,6 +178,7 @@ struct BlockArgs {
   float* W_hat;
   float* row_loss;
   int64_t n_groups;
+  int vec_u;      // U is 16-byte aligned and c % 4 == 0
 };
 
 // Fit the ruler of the group starting at block column j on the current
@@ -202,52 +209,84 @@ GPTQ_DEV void fit_group(const float (&w)[S], int p, int j, int Bw, int64_t g, in
   fit_ruler(mn, mx, maxq, scale, zero);
 }
 
-// MIDGROUPS: groups shorter than the block also start inside it.  FULL: the
-// block has all BMAX columns (no per-step bound check, so the compiler can
-// schedule LDS reads of later steps early).
-template <int L, bool MIDGROUPS, bool FULL>
-__global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
-  constexpr int S = BMAX / L;          // slots per lane
-  constexpr int ROWS = 256 / L;        // rows per workgroup
-  constexpr int SP = S, URS = BMAX;  // Ul[j][p*S + m] = U[j][p + L m]
-  __shared__ __attribute__((aligned(16))) float Ul[BMAX * URS];
-  __shared__ float invd[BMAX];
-
+// Stage V[j][k] = U[i1 + j][i1 + k] / U[i1 + j][i1 + j] for k > j (0 on and
+// left of the diagonal and past Bw) row-major in LDS, and invd[j] = 1 / U_jj.
+// With the repairs written as w_k -= err_j * V[j][k], err_j = w_j - w_hat_j,
+// the division by the diagonal leaves the column-to-column dependency chain,
+// and the zero diagonal leaves each column's register holding the value it
+// had when its turn came.
+GPTQ_DEV void stage_block(const BlockArgs& a, float* Vl, float* invd, bool full) {
   const int tid = threadIdx.x;
-  const int p = tid % L;
-  const int64_t row = (int64_t)blockIdx.x * ROWS + tid / L;
-  const bool valid = row < a.r;
-  const int Bw = FULL ? BMAX : a.Bw;
+  const int Bw = a.Bw;
   const int64_t i1 = a.i1, c = a.c;
-  const float* Wrow = a.Wp + (valid ? row : 0) * c;
-
-  // Stage the block's corner of U: zero left of the diagonal and past Bw.
-  for (int e = tid; e < BMAX * BMAX; e += 256) {
-    const int j = e / BMAX, k = e % BMAX;
-    float v = 0.f;
-    if (j < Bw && k < Bw && k >= j) v = a.U[(i1 + j) * c + (i1 + k)];
-    Ul[j * URS + (k % L) * SP + (k / L)] = v;
-  }
-  if (tid < BMAX) invd[tid] = tid < Bw ? __fdiv_rn(1.0f, a.U[(i1 + tid) * c + (i1 + tid)]) : 0.f;
-
-  float w[S];
+  if (full && a.vec_u) {
+    // thread t, load u: row j = t / 32 + 8 u, columns 4 (t % 32) .. +3
+    floatx4 v[16];
+    const float* ub = a.U + (i1 + (tid >> 5)) * c + i1 + (tid & 31) * 4;
 #pragma unroll
-  for (int m = 0; m < S; ++m) {
-    const int col = p + L * m;
-    w[m] = (valid && col < Bw) ? Wrow[i1 + col] : 0.f;
+    for (int u = 0; u < 16; ++u) v[u] = *reinterpret_cast<const floatx4*>(ub + (int64_t)(8 * u) * c);
+    if (tid < BMAX) invd[tid] = __fdiv_rn(1.0f, a.U[(i1 + tid) * c + (i1 + tid)]);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e4 = tid + 256 * u, j = e4 >> 5, k = (e4 & 31) * 4;
+      const float sj = invd[j];
+      floatx4 o;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) o[cc] = (k + cc > j) ? v[u][cc] * sj : 0.f;
+      *reinterpret_cast<floatx4*>(Vl + j * BMAX + k) = o;
+    }
+  } else {
+    if (tid < BMAX) invd[tid] = tid < Bw ? __fdiv_rn(1.0f, a.U[(i1 + tid) * c + (i1 + tid)]) : 0.f;
+    __syncthreads();
+    for (int e = tid; e < BMAX * BMAX; e += 256) {
+      const int j = e / BMAX, k = e % BMAX;
+      float v = 0.f;
+      if (j < Bw && k < Bw && k > j) v = a.U[(i1 + j) * c + (i1 + k)] * invd[j];
+      Vl[e] = v;
+    }
   }
   __syncthreads();
+}
 
+// The tick offset dq = q - zero of the value x: clamp(rne(t) + zero, 0, maxq)
+// - zero = med3(rne(t), -zero, maxq - zero), zero being a whole number, with
+// t = x / scale correctly rounded (EXACT) or t = x * (1/scale).
+template <bool EXACT>
+GPTQ_DEV float tick(float x, float scale, float y, float lo, float hi) {
+  float t;
+  if constexpr (EXACT) {
+    t = div_by_recip(x, scale, y);
+    t = __builtin_fmaf(__builtin_fmaf(-t, scale, x), y, t);
+  } else {
+    t = __fmul_rn(x, y);
+  }
+  return __builtin_amdgcn_fmed3f(rne(t), lo, hi);
+}
+
+// True when t = x * (1/scale) lies within 2^-21 |t| of a half-integer, where
+// the correctly rounded quotient x / scale (|t - x/scale| < 2^-22.4 |t|) might
+// round to the other neighbour.
+GPTQ_DEV bool near_half(float x, float y) {
+  const float t = __fmul_rn(x, y);
+  const float d = __fsub_rn(t, rne(t));
+  return fabsf(d) >= __builtin_fmaf(-fabsf(t), 0x1p-21f, 0.5f);
+}
+
+// Ruler of the block's first column: per row (read), fitted here (group
+// starting at the block), or continued from an earlier block (read).
+template <int L, int S>
+GPTQ_DEV void block_ruler(const BlockArgs& a, const float (&w)[S], int p, int64_t row, bool valid, int Bw,
+                          const float* Wrow, float& scale, float& zero) {
+  const int64_t g = a.groupsize, i1 = a.i1;
   const float maxq = (float)((1 << a.bits) - 1);
-  const int64_t g = a.groupsize;
-  float scale = 1.f, zero = 0.f;
   if (g <= 0) {
     if (valid) {
       scale = a.scales[row * a.n_groups];
       zero = (float)a.zeros[row * a.n_groups];
     }
   } else if (i1 % g == 0) {
-    fit_group<L, S>(w, p, 0, Bw, g, i1, c, Wrow, valid, maxq, scale, zero);
+    fit_group<L, S>(w, p, 0, Bw, g, i1, a.c, Wrow, valid, maxq, scale, zero);
     if (valid && p == 0) {
       a.scales[row * a.n_groups + i1 / g] = scale;
       a.zeros[row * a.n_groups + i1 / g] = (int32_t)zero;
@@ -258,21 +297,59 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
     scale = a.scales[row * a.n_groups + i1 / g];
     zero = (float)a.zeros[row * a.n_groups + i1 / g];
   }
+}
+
+// The block's columns in order, for the L lanes of each row (see the file
+// header for the lane mapping).  On return w[m] holds, for every column of
+// the block, its value when its turn came (V's zero diagonal leaves it
+// alone afterwards).  With MIDGROUPS the ruler changes inside the block, so
+// the tick offset, w_hat and error of each column are recorded as they are
+// taken, and the fast pass's doubtful decisions are collected per step;
+// otherwise everything is recomputed from w after the loop.  EXACT == false
+// decides with t = x * (1/scale); an unflagged fast pass is bitwise the exact
+// pass, because every later value depends on the decision only.
+template <int L, bool MIDGROUPS, bool FULL, bool EXACT>
+GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row, bool valid,
+                        const float* Wrow, float (&w)[BMAX / L], float (&qreg)[BMAX / L],
+                        float (&ereg)[BMAX / L], float (&whreg)[BMAX / L], float& scale, float& zero) {
+  constexpr int S = BMAX / L;
+  const int Bw = FULL ? BMAX : a.Bw;
+  const int64_t i1 = a.i1, c = a.c;
+  const float maxq = (float)((1 << a.bits) - 1);
+  const int64_t g = a.groupsize;
+  block_ruler<L, S>(a, w, p, row, valid, Bw, Wrow, scale, zero);
   float y = __fdiv_rn(1.0f, scale);
-  float qreg[S], whreg[S], ereg[S];
-#pragma unroll
-  for (int m = 0; m < S; ++m) qreg[m] = whreg[m] = ereg[m] = 0.f;
-  float loss = 0.f;
+  float lo = -zero, hi = maxq - zero;
+  uint64_t bad = 0;
   int next_group = MIDGROUPS ? (int)g : BMAX;
+  // Lanes of the rows' owners of block column j: lane j % L of every row.
+  constexpr uint64_t OWN0 = L == 16 ? 0x0001000100010001ull : 0x1111111111111111ull;
+
+  // Rows of V are read two steps ahead into a ring of registers; the
+  // scheduling barrier at the end of each step keeps the compiler from
+  // hoisting every read of the unrolled loop to the top (and spilling).
+  float vb[3][S];
+  const float* vcol = Vl + p;
+  auto fetch = [&](int jj, float (&dst)[S]) {
+#pragma unroll
+    for (int m = 0; m < S; ++m)
+      if (m >= jj / L) dst[m] = vcol[jj * BMAX + L * m];
+  };
+  fetch(0, vb[0]);
+  fetch(1, vb[1]);
 
 #pragma clang loop unroll(full)
   for (int j = 0; j < BMAX; ++j) {
-    if (!FULL && j >= Bw) continue;
+    if (j + 2 < BMAX) fetch(j + 2, vb[(j + 2) % 3]);
+    // A short block runs all BMAX steps: its missing columns hold 0 in w and
+    // in V, quantize to an error of exactly 0 and are never stored.
     const int mj = j / L, pj = j % L;
     if constexpr (MIDGROUPS) {
-      if (j > 0 && j == next_group) {
+      if (j > 0 && j == next_group && (FULL || j < Bw)) {
         fit_group<L, S>(w, p, j, Bw, g, i1, c, Wrow, valid, maxq, scale, zero);
         y = __fdiv_rn(1.0f, scale);
+        lo = -zero;
+        hi = maxq - zero;
         if (valid && p == 0) {
           const int64_t gi = (i1 + j) / g;
           a.scales[row * a.n_groups + gi] = scale;
@@ -281,28 +358,99 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
         next_group += (int)g;
       }
     }
-    // Quantize column j (meaningful on the owner lane pj): the quotient is the
-    // correctly rounded x / scale (two FMA corrections of x * (1/scale)).
     const float x = w[mj];
-    float t = div_by_recip(x, scale, y);
-    t = __builtin_fmaf(__builtin_fmaf(-t, scale, x), y, t);
-    const float q = fminf(fmaxf(rne(t) + zero, 0.f), maxq);
-    const float wh = __fmul_rn(scale, q - zero);
-    const float e = __fmul_rn(x - wh, invd[j]);
-    const bool own = (p == pj);
-    qreg[mj] = own ? q : qreg[mj];
-    whreg[mj] = own ? wh : whreg[mj];
-    ereg[mj] = own ? e : ereg[mj];
-    loss = own ? __builtin_fmaf(0.5f * e, e, loss) : loss;
-    // Repair every later column of the block: w_k -= e * U[j][k].
-    const float eb = bcast<L>(e, pj);
-    const float* urow = Ul + j * URS + p * SP;
+    const float dq = tick<EXACT>(x, scale, y, lo, hi);
+    const float err = __builtin_fmaf(-scale, dq, x);   // w - scale * (q - zero)
+    if constexpr (MIDGROUPS) {
+      const bool own = (p == pj);
+      qreg[mj] = own ? dq + zero : qreg[mj];
+      whreg[mj] = own ? __fmul_rn(scale, dq) : whreg[mj];
+      ereg[mj] = own ? err : ereg[mj];
+      if constexpr (!EXACT) {
+        bad |= __ballot(near_half(x, y)) & (OWN0 << pj);
+        asm volatile("" : "+s"(bad));
+      }
+      // Materialise this step's records here: left alone, the compiler sinks
+      // every step's selects past the loop and keeps all operands live.
+      asm volatile("" : "+v"(qreg[mj]), "+v"(ereg[mj]), "+v"(whreg[mj]));
+    }
+    // Repair every later column of the block: w_k -= err * V[j][k].
+    const float eb = bcast<L>(err, pj);
 #pragma unroll
     for (int m = 0; m < S; ++m) {
-      if (m >= mj) w[m] = __builtin_fmaf(-eb, urow[m], w[m]);
+      if (m >= mj) w[m] = __builtin_fmaf(-eb, vb[j % 3][m], w[m]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return bad != 0;
+}
+
+// MIDGROUPS: groups shorter than the block also start inside it.  FULL: the
+// block has all BMAX columns.
+template <int L, bool MIDGROUPS, bool FULL>
+__global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
+  constexpr int S = BMAX / L;          // slots per lane
+  constexpr int ROWS = 256 / L;        // rows per workgroup
+  __shared__ __attribute__((aligned(16))) float Vl[BMAX * BMAX];
+  __shared__ float invd[BMAX];
+
+  const int tid = threadIdx.x;
+  const int p = tid % L;
+  const int64_t row = (int64_t)blockIdx.x * ROWS + tid / L;
+  const bool valid = row < a.r;
+  const int Bw = FULL ? BMAX : a.Bw;
+  const int64_t i1 = a.i1, c = a.c;
+  const float* Wrow = a.Wp + (valid ? row : 0) * c;
+  const float maxq = (float)((1 << a.bits) - 1);
+
+  float w[S];
+  auto load_w = [&]() {
+#pragma unroll
+    for (int m = 0; m < S; ++m) {
+      const int col = p + L * m;
+      w[m] = (valid && col < Bw) ? Wrow[i1 + col] : 0.f;
+    }
+  };
+  load_w();
+  stage_block(a, Vl, invd, FULL);
+
+  float qreg[S], ereg[S], whreg[S];
+#pragma unroll
+  for (int m = 0; m < S; ++m) qreg[m] = ereg[m] = whreg[m] = 0.f;
+  float scale = 1.f, zero = 0.f;
+  bool bad = run_chain<L, MIDGROUPS, FULL, false>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
+  if constexpr (!MIDGROUPS) {
+    const float y = __fdiv_rn(1.0f, scale);
+#pragma unroll
+    for (int m = 0; m < S; ++m) bad = bad || near_half(w[m], y);
+  }
+  const bool exact = __ballot(bad) != 0;   // wave-uniform
+  if (exact) {                              // repeat this wave's rows exactly
+    load_w();
+    run_chain<L, MIDGROUPS, FULL, true>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
+  }
+  if constexpr (!MIDGROUPS) {
+    // Codes, w_hat and errors from the values the columns had at their turn.
+    const float y = __fdiv_rn(1.0f, scale);
+    const float lo = -zero, hi = maxq - zero;
+#pragma unroll
+    for (int m = 0; m < S; ++m) {
+      const float dq = exact ? tick<true>(w[m], scale, y, lo, hi) : tick<false>(w[m], scale, y, lo, hi);
+      qreg[m] = dq + zero;
+      whreg[m] = __fmul_rn(scale, dq);
+      ereg[m] = __builtin_fmaf(-scale, dq, w[m]);
     }
   }
 
+  float loss = 0.f;
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    const int col = p + L * m;
+    if (col < Bw) {
+      ereg[m] *= invd[col];                      // e = (w - w_hat) / U_jj
+      loss = __builtin_fmaf(0.5f * ereg[m], ereg[m], loss);
+    }
+  }
   loss = row_sum<L>(loss);
   if (!valid) return;
 #pragma unroll
@@ -313,7 +461,7 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
       const int64_t orig = a.perm ? clamp_col(a.perm[pk], c) : pk;
       a.codes[row * c + orig] = (uint8_t)(int)qreg[m];
       if (a.W_hat) a.W_hat[row * c + orig] = whreg[m];
-      a.Et[(int64_t)col * a.r + row] = ereg[m];
+      a.E[row * a.lde + col] = ereg[m];
     }
   }
   if (p == 0 && a.row_loss) a.row_loss[row] += loss;
@@ -342,16 +490,16 @@ int64_t super_block(int64_t B, int64_t g) {
   return B;
 }
 
-void gemm_update(hipStream_t s, int64_t r, int64_t c, const float* Et, int K, const float* U, int64_t k0,
-                 int64_t n0, int64_t n1, float* Wp) {
-  // Wp[:, n0:n1] -= E * U[k0:k0+K, n0:n1], E stored K x r (row k = column k of E)
+void gemm_update(hipStream_t s, int64_t r, int64_t c, const float* E, int64_t lde, int K, const float* U,
+                 int64_t k0, int64_t n0, int64_t n1, float* Wp) {
+  // Wp[:, n0:n1] -= E[:, 0:K] * U[k0:k0+K, n0:n1], E row-major with row stride lde
   GemmArgs gm;
   gm.M = (int)r;
   gm.N = (int)(n1 - n0);
   gm.K = K;
-  gm.A = Et;
-  gm.lda = r;
-  gm.a_trans = 1;
+  gm.A = E;
+  gm.lda = lde;
+  gm.a_trans = 0;
   gm.a_mask = MASK_NONE;
   gm.a_off = 0;
   gm.B = U + k0 * c + n0;
@@ -372,7 +520,8 @@ void gemm_update(hipStream_t s, int64_t r, int64_t c, const float* Et, int K, co
 void launch_quantize(const QuantArgs& a, hipStream_t s) {
   const int64_t r = a.r, c = a.c;
   float* Wp = reinterpret_cast<float*>(a.ws);
-  float* Et = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + align256((size_t)r * c * sizeof(float)));
+  // E: r x SB row-major, the scaled errors of the current super-block
+  float* E = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + align256((size_t)r * c * sizeof(float)));
   hipLaunchKernelGGL(init_kernel, dim3((unsigned)r), dim3(256), 0, s, a, Wp);
   hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, s, a.perm, c,
                      a.groupsize, a.g_idx);
@@ -390,8 +539,10 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   b.W_hat = a.W_hat;
   b.row_loss = a.row_loss;
   b.n_groups = a.groupsize > 0 ? (c + a.groupsize - 1) / a.groupsize : 1;
+  b.vec_u = ((c & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.U) & 15) == 0);
   const int64_t B = a.blocksize;
   const int64_t SB = super_block(B, a.groupsize);
+  b.lde = SB;
   // 16 lanes per row when there are enough rows to fill the chip that way.
   const bool wide = r * 16 >= 256 * 64;
   const bool mid = a.groupsize > 0 && a.groupsize < B;
@@ -403,7 +554,7 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
       const int64_t i2 = i1 + Bw;
       b.i1 = i1;
       b.Bw = Bw;
-      b.Et = Et + (i1 - s1) * r;
+      b.E = E + (i1 - s1);
       const bool full = Bw == BMAX;
 #define GPTQ_BLOCK(LL, MID, FU, G) hipLaunchKernelGGL((block_kernel<LL, MID, FU>), G, dim3(256), 0, s, b)
       if (wide) {
@@ -415,10 +566,10 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
       }
 #undef GPTQ_BLOCK
       // repairs of this block's errors to the rest of the super-block, at once
-      if (i2 < s2) gemm_update(s, r, c, b.Et, Bw, a.U, i1, i2, s2, Wp);
+      if (i2 < s2) gemm_update(s, r, c, b.E, SB, Bw, a.U, i1, i2, s2, Wp);
     }
     // repairs of the whole super-block to every later column, deferred to here
-    if (s2 < c) gemm_update(s, r, c, Et, (int)(s2 - s1), a.U, s1, s2, c, Wp);
+    if (s2 < c) gemm_update(s, r, c, E, SB, (int)(s2 - s1), a.U, s1, s2, c, Wp);
   }
 }
 
