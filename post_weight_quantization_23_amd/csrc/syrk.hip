@@ -116,71 +116,59 @@ GPTQ_DEV floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c) {
   }
 }
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(512, 1) void syrk16_kernel(const uint16_t* __restrict__ X, int64_t ldx,
-                                                         int64_t n_tok, int d, int nt,
-                                                         int64_t chunk, float* __restrict__ H,
-                                                         float* __restrict__ part, int tiles,
-                                                         int splits, int* __restrict__ counters,
-                                                         int per_xcd) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // LDS: A buffers 0/1 then B buffers 0/1, TILE rows of ROWB bytes each.
+// The K-loop of one tile over tokens [t_beg, t_end).  FAST: the tile's
+// feature slabs lie inside [0, d) and X is 16-byte aligned with ldx % 8 == 0,
+// so every patch row is one buffer load; rows past t_end fall outside the
+// descriptor's records and load zeros.  Otherwise the patches go through the
+// bounds-checked loader.  The two variants are separate loops, so no
+// register copies sit between the issue of a load and its use.
+//
+// Software pipeline over K-steps of 64 tokens: at the start of step s the
+// registers hold the raw patches of step s+1.  They are transposed into the
+// LDS buffer that step s's MFMAs do not read, and the loads of step s+2 are
+// issued into the freed registers, before step s's MFMAs (LDS buffer s&1).
+// MFMA operands of the next 16-token sub-step are read from LDS while the
+// current sub-step's MFMAs run.
+template <int DT, bool VEC, bool FAST, bool DIAG>
+GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_beg, int64_t t_end, int d,
+                         int fi0, int fj0, bool compute_lower, int wm, int wn, unsigned char* smem,
+                         floatx16 (&acc)[4][4]) {
+  constexpr bool diag = DIAG;
+  const bool compute = !DIAG || compute_lower;
   auto a_buf = [&](int b) { return smem + b * (TILE * ROWB); };
   auto b_buf = [&](int b) { return smem + (2 + b) * (TILE * ROWB); };
-
-  int tile, split;
-  if (!work_unit(blockIdx.x, tiles, splits, per_xcd, tile, split)) return;
-  int bi, bj;
-  tile_coords(tile, nt, bi, bj);
-  const bool diag = bi == bj;
-  const int fi0 = bi * TILE, fj0 = bj * TILE;
-  const int64_t t_beg = (int64_t)split * chunk;
-  const int64_t t_end = min(n_tok, t_beg + chunk);
-
-  // 8 waves as 2 (rows) x 4 (columns) of 128 x 64 output blocks.
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
-  // Loader role: threads 0..255 carry patches of the row slab (A), threads
-  // 256..511 patches of the column slab (B, not needed on diagonal tiles).
-  const bool is_b = tid >= 256;
-  const int ptid = tid & 255;
-  const int tb = ptid >> 5, fb = ptid & 31;
-  const int f_slab = is_b ? fj0 : fi0;
-  const bool loads = !(is_b && diag);
-
-  floatx16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // Software pipeline over K-steps of 64 tokens with one register set: at the
-  // start of step s the registers hold the raw patch of step s+1.  During the
-  // first half of step s's MFMAs (LDS buffer s&1) that patch is transposed
-  // into the other LDS buffer; the loads of step s+2 are then issued into the
-  // freed registers and have the rest of step s and the start of step s+1 to
-  // arrive.
-  u32x4 rg[8];
-  const bool inside = VEC && (fi0 + TILE <= d) && (fj0 + TILE <= d);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Loader role: every thread carries one 8-token x 8-feature patch of the
+  // row slab (A) and one of the column slab (B, not needed on diagonal tiles).
+  const int tb = tid >> 5, fb = tid & 31;
+  u32x4 ra[8], rb[8];
   const int64_t nsteps = (t_end - t_beg + KSTEP - 1) / KSTEP;
+  // byte offset of the thread's patch inside a token row
+  const int off_a = 2 * (fi0 + fb * 8), off_b = 2 * (fj0 + fb * 8);
 
   auto fetch = [&](int64_t st) {
-    if (!loads) return;
     const int64_t t0 = t_beg + st * KSTEP + tb * 8;
-    if (inside && t_beg + (st + 1) * KSTEP <= t_end) {
-      const uint16_t* pa = X + t0 * ldx + f_slab + fb * 8;
+    if constexpr (FAST) {
+      // One descriptor per K-step (wave-uniform): base at the step's first
+      // token row, records up to t_end, so rows past t_end load zeros.  The
+      // thread's row and feature offset go in the VGPR offset.
+      const int64_t ts = t_beg + st * KSTEP;
+      const int64_t nrec = min((t_end - ts) * ldx * 2, (int64_t)0x7fffffff);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(X + ts * ldx), (short)0, (int)nrec, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rg[i] = *reinterpret_cast<const u32x4*>(pa + i * ldx);
+      for (int i = 0; i < 8; ++i) {
+        const int ro = (tb * 8 + i) * (int)ldx * 2;
+        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ro + off_a, 0, 0));
+        if (!diag) rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ro + off_b, 0, 0));
+      }
     } else {
-      load_patch<VEC>(X, ldx, t0, t_end, f_slab + fb * 8, d, rg);
+      load_patch<VEC>(X, ldx, t0, t_end, fi0 + fb * 8, d, ra);
+      if (!diag) load_patch<VEC>(X, ldx, t0, t_end, fj0 + fb * 8, d, rb);
     }
   };
-  // Transpose rows m0 .. m0+3 of the patch and write them to LDS.
-  auto stage4 = [&](int buf, int m0) {
-    if (!loads) return;
-    unsigned char* lds = is_b ? b_buf(buf) : a_buf(buf);
+  // Transpose feature rows m0 .. m0+3 of a patch and write them to LDS.
+  auto stage4 = [&](unsigned char* lds, const u32x4 (&rg)[8], int m0) {
 #pragma unroll
     for (int m = m0; m < m0 + 4; ++m) {
       const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
@@ -191,29 +179,35 @@ __global__ __launch_bounds__(512, 1) void syrk16_kernel(const uint16_t* __restri
       *reinterpret_cast<u32x4*>(lds + f * ROWB + ((tb ^ swz(f)) * 16)) = o;
     }
   };
-  auto mfma_kk = [&](const unsigned char* as, const unsigned char* bs, int kk) {
+  auto stage_half = [&](int buf, int m0) {
+    stage4(a_buf(buf), ra, m0);
+    if (!diag) stage4(b_buf(buf), rb, m0);
+  };
+  u32x4 fa[2][4], fbm[2][4];
+  auto frags = [&](const unsigned char* as, const unsigned char* bs, int kk, u32x4 (&a)[4], u32x4 (&b)[4]) {
     const int chunk_id = 2 * kk + (lane >> 5);
-    u32x4 a[4], b[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int f = wm + 32 * i + (lane & 31);
       a[i] = *reinterpret_cast<const u32x4*>(as + f * ROWB + ((chunk_id ^ swz(f)) * 16));
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const int f = wn + 32 * j + (lane & 31);
       b[j] = *reinterpret_cast<const u32x4*>(bs + f * ROWB + ((chunk_id ^ swz(f)) * 16));
     }
+  };
+  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<DT>(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<DT>(a[i], b[j], acc[i][j]);
   };
 
   if (nsteps > 0) {
     fetch(0);
-    stage4(0, 0);
-    stage4(0, 4);
+    stage_half(0, 0);
+    stage_half(0, 4);
     if (nsteps > 1) fetch(1);
     __syncthreads();
     int buf = 0;
@@ -221,45 +215,103 @@ __global__ __launch_bounds__(512, 1) void syrk16_kernel(const uint16_t* __restri
       const bool stage_next = st + 1 < nsteps;
       const unsigned char* as = a_buf(buf);
       const unsigned char* bs = diag ? a_buf(buf) : b_buf(buf);
-      mfma_kk(as, bs, 0);
-      if (stage_next) stage4(buf ^ 1, 0);
-      mfma_kk(as, bs, 1);
-      if (stage_next) stage4(buf ^ 1, 4);
+      if (compute) {
+        frags(as, bs, 0, fa[0], fbm[0]);
+        frags(as, bs, 1, fa[1], fbm[1]);
+      }
+      // Transpose step st+1 into the other buffer and issue the loads of
+      // step st+2 first, so that they have a whole step to arrive.
+      if (stage_next) {
+        stage_half(buf ^ 1, 0);
+        stage_half(buf ^ 1, 4);
+      }
       if (st + 2 < nsteps) fetch(st + 2);
-      mfma_kk(as, bs, 2);
-      mfma_kk(as, bs, 3);
+      if (compute) {
+        mfmas(fa[0], fbm[0]);
+        frags(as, bs, 2, fa[0], fbm[0]);
+        mfmas(fa[1], fbm[1]);
+        frags(as, bs, 3, fa[1], fbm[1]);
+        mfmas(fa[0], fbm[0]);
+        mfmas(fa[1], fbm[1]);
+      }
       __syncthreads();
       buf ^= 1;
     }
   }
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                         int64_t n_tok, int d, int nt,
+                                                         int64_t chunk, float* __restrict__ H,
+                                                         float* __restrict__ part, int tiles,
+                                                         int splits, int* __restrict__ counters,
+                                                         int per_xcd) {
+  // LDS: A buffers 0/1 then B buffers 0/1, TILE rows of ROWB bytes each.
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  int tile, split;
+  if (!work_unit(blockIdx.x, tiles, splits, per_xcd, tile, split)) return;
+  int bi, bj;
+  tile_coords(tile, nt, bi, bj);
+  const bool diag = bi == bj;
+  const int fi0 = bi * TILE, fj0 = bj * TILE;
+  const int64_t t_beg = (int64_t)split * chunk;
+  const int64_t t_end = min(n_tok, t_beg + chunk);
+
+  // 4 waves as 2 x 2 blocks of 128 x 128 (4 x 4 MFMA blocks of 32 x 32 each,
+  // accumulators in the AGPR half of the register file).  On a diagonal tile
+  // the lower-left block mirrors the upper-right one and is not computed.
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const bool compute = !(diag && wm > wn);
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const bool fast = VEC && fi0 + TILE <= d && fj0 + TILE <= d;
+#define GPTQ_STEPS(F, D) syrk_steps<DT, VEC, F, D>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc)
+  if (fast) {
+    if (diag) GPTQ_STEPS(true, true); else GPTQ_STEPS(true, false);
+  } else {
+    if (diag) GPTQ_STEPS(false, true); else GPTQ_STEPS(false, false);
+  }
+#undef GPTQ_STEPS
 
   // Epilogue.  Lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] per block.
   if (part == nullptr) {
+    if (compute) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int gj = fj0 + wn + 32 * j + (lane & 31);
+        for (int j = 0; j < 4; ++j) {
+          const int gj = fj0 + wn + 32 * j + (lane & 31);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int gi = fi0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (gi < d && gj < d) {
-            float* p = H + (int64_t)gi * d + gj;
-            *p = __builtin_fmaf(2.0f, acc[i][j][v], *p);
+          for (int v = 0; v < 16; ++v) {
+            const int gi = fi0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (gi < d && gj < d) {
+              float* p = H + (int64_t)gi * d + gj;
+              *p = __builtin_fmaf(2.0f, acc[i][j][v], *p);
+            }
           }
         }
-      }
+    }
   } else {
     float* pt = part + ((int64_t)split * tiles + tile) * (TILE * TILE);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const int c = wn + 32 * j + (lane & 31);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          pt[r * TILE + c] = acc[i][j][v];
+          pt[r * TILE + c] = compute ? acc[i][j][v] : 0.f;
         }
       }
     // The last of the tile's `splits` workgroups to finish sums all partials
@@ -272,7 +324,7 @@ __global__ __launch_bounds__(512, 1) void syrk16_kernel(const uint16_t* __restri
     if (!last) return;
     __threadfence();
     const float* p0 = part + (int64_t)tile * (TILE * TILE);
-    for (int e4 = tid; e4 < TILE * TILE / 4; e4 += 512) {
+    for (int e4 = tid; e4 < TILE * TILE / 4; e4 += 256) {
       const int r = e4 / (TILE / 4), c = (e4 % (TILE / 4)) * 4;
       floatx4 sum = {0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < splits; ++k)
@@ -354,7 +406,7 @@ void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok,
   const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
   const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
 #define GPTQ_SYRK_LAUNCH(DT, V)                                                                        \
-  hipLaunchKernelGGL((syrk16_kernel<DT, V>), grid, dim3(512), shmem, s, Xh, ldx, n_tok, (int)d, nt, \
+  hipLaunchKernelGGL((syrk16_kernel<DT, V>), grid, dim3(256), shmem, s, Xh, ldx, n_tok, (int)d, nt, \
                      p.chunk, H, part, p.tiles, p.splits, counters, per_xcd)
   if (dtype == 1) {
     if (vec) GPTQ_SYRK_LAUNCH(1, true); else GPTQ_SYRK_LAUNCH(1, false);
