@@ -15,7 +15,9 @@
 //
 // Tiling: TM x TN output tile per 256-thread workgroup, 2 x 2 waves, each
 // wave (TM/2) x (TN/2) as 32x32 MFMA blocks; K-steps of KT staged through LDS
-// in k-major rows (As[k][m], Bs[k][n]) with double buffering.
+// in k-major rows (As[k][m], Bs[k][n]) with double buffering.  One launch may
+// carry two independent problems: workgroups past the first problem's tiles
+// work on the second.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,8 +58,13 @@ GPTQ_DEV floatx4 load4(const float* base, int64_t ld, int row, int col, int rows
   return v;
 }
 
+struct GemmPair {
+  GemmArgs g[2];
+  int tiles0;   // tiles of g[0]; workgroups from here on belong to g[1]
+};
+
 template <int TM, int TN, int KT>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmPair pr) {
   constexpr int WM = TM / 2, WN = TN / 2;   // per-wave tile
   constexpr int MB = WM / 32, NB = WN / 32; // 32x32 blocks per wave
   constexpr int LDA_S = TM + PAD, LDB_S = TN + PAD;
@@ -66,8 +73,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   auto As = [&](int b) { return gemm_smem + b * (KT * LDA_S); };
   auto Bs = [&](int b) { return gemm_smem + 2 * (KT * LDA_S) + b * (KT * LDB_S); };
 
+  const bool second = (int)blockIdx.x >= pr.tiles0;
+  const GemmArgs& g = second ? pr.g[1] : pr.g[0];
+  const int bid = second ? (int)blockIdx.x - pr.tiles0 : (int)blockIdx.x;
   const int tiles_n = (g.N + TN - 1) / TN;
-  const int bm = blockIdx.x / tiles_n, bn = blockIdx.x % tiles_n;
+  const int bm = bid / tiles_n, bn = bid % tiles_n;
   const int m0 = bm * TM, n0 = bn * TN;
   if (g.upper_only && n0 + TN <= m0) return;  // tile strictly below the diagonal
 
@@ -221,7 +231,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 template <int TM, int TN, int KT>
-void launch_tile(const GemmArgs& g, hipStream_t s) {
+int64_t tiles_of(const GemmArgs& g) {
+  return (g.M <= 0 || g.N <= 0) ? 0 : (int64_t)((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
+}
+
+template <int TM, int TN, int KT>
+void launch_tile(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
   constexpr size_t smem = (size_t)2 * KT * ((TM + PAD) + (TN + PAD)) * sizeof(float);
   static bool attr = false;
   if (!attr) {
@@ -229,21 +244,32 @@ void launch_tile(const GemmArgs& g, hipStream_t s) {
                               (int)smem);
     attr = true;
   }
-  const int64_t tiles = (int64_t)((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
-  hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, KT>), dim3((unsigned)tiles), dim3(256), smem, s, g);
+  GemmPair pr;
+  pr.g[0] = g0;
+  pr.g[1] = g1 ? *g1 : g0;
+  const int64_t t0 = tiles_of<TM, TN, KT>(g0);
+  const int64_t t1 = g1 ? tiles_of<TM, TN, KT>(*g1) : 0;
+  pr.tiles0 = (int)t0;
+  if (t0 + t1 == 0) return;
+  hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, KT>), dim3((unsigned)(t0 + t1)), dim3(256), smem, s, pr);
+}
+
+void launch_dispatch(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
+  // 128 x 128 tiles when that already gives enough workgroups, else 64 x 64.
+  const int64_t t128 = tiles_of<128, 128, 32>(g0) + (g1 ? tiles_of<128, 128, 32>(*g1) : 0);
+  if (t128 >= 480) {
+    launch_tile<128, 128, 32>(g0, g1, s);
+  } else {
+    launch_tile<64, 64, 32>(g0, g1, s);
+  }
 }
 
 }  // namespace
 
-// Tile choice: 128 x 128 when that already gives enough workgroups, else 64 x 64.
-void launch_gemm_f32(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return;
-  const int64_t t128 = (int64_t)((g.M + 127) / 128) * ((g.N + 127) / 128);
-  if (t128 >= 480) {
-    launch_tile<128, 128, 32>(g, s);
-  } else {
-    launch_tile<64, 64, 32>(g, s);
-  }
+void launch_gemm_f32(const GemmArgs& g, hipStream_t s) { launch_dispatch(g, nullptr, s); }
+
+void launch_gemm_f32_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s) {
+  launch_dispatch(g0, &g1, s);
 }
 
 }  // namespace gptq

@@ -22,6 +22,9 @@ struct GemmArgs {
   int upper_only;
 };
 void launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+// Two independent products in one launch (one grid, the second problem's
+// tiles after the first's).
+void launch_gemm_f32_pair(const GemmArgs& g0, const GemmArgs& g1, hipStream_t s);
 
 // --- Hessian (syrk.hip) ---
 struct SyrkPlan {

@@ -298,19 +298,21 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* H, int64_t d, int64_t 
 
 constexpr size_t leaf_smem_bytes() { return (size_t)LEAF_FLOATS * sizeof(float); }
 
-void gemm(hipStream_t s, int M, int N, int K, const float* A, int64_t lda, int at, int am,
-          const float* B, int64_t ldb, int bt, int bm, float* C, int64_t ldc, float alpha, float beta,
-          int upper_only) {
+GemmArgs gemm_args(int M, int N, int K, const float* A, int64_t lda, int at, int am, const float* B, int64_t ldb,
+                   int bt, int bm, float* C, int64_t ldc, float alpha, float beta, int upper_only) {
   GemmArgs g;
   g.M = M; g.N = N; g.K = K;
   g.A = A; g.lda = lda; g.a_trans = at; g.a_mask = am; g.a_off = 0;
   g.B = B; g.ldb = ldb; g.b_trans = bt; g.b_mask = bm; g.b_off = 0;
   g.C = C; g.ldc = ldc; g.alpha = alpha; g.beta = beta; g.upper_only = upper_only;
-  launch_gemm_f32(g, s);
+  return g;
 }
 
-// Recursive U for the diagonal block (o, n) of H; Wk is a d x d scratch
-// matrix whose upper-right block positions hold each node's temporary.
+// Recursive U for the diagonal block (o, n) of H.  Wk is a d x d scratch
+// matrix: each node keeps T in its upper-right block position and X^T in its
+// lower-left one, so nodes never share scratch.  With U12 = -U11 (T U22), the
+// product X = T U22 needs only T and U22 and shares one launch with the
+// update of A; U12 is then written straight into H.
 void factor_rec(float* H, float* Wk, int64_t d, int64_t o, int64_t n, int32_t* info, hipStream_t s) {
   if (n <= NB) {
     hipLaunchKernelGGL(leaf_kernel, dim3(1), dim3(256), leaf_smem_bytes(), s, H, d, o, (int)n, info);
@@ -323,19 +325,17 @@ void factor_rec(float* H, float* Wk, int64_t d, int64_t o, int64_t n, int32_t* i
   float* B = H + o * d + (o + n1);
   float* C = H + (o + n1) * d + (o + n1);
   float* T = Wk + o * d + (o + n1);
+  float* Xt = Wk + (o + n1) * d + o;   // n2 x n1
   factor_rec(H, Wk, d, o + n1, n2, info, s);
   // T = B * U22^T : op(B) = U22^T, stored as U22 [n][k] -> b_trans, keep k >= n
-  gemm(s, (int)n1, (int)n2, (int)n2, B, d, 0, MASK_NONE, C, d, 1, MASK_LOWER, T, d, 1.f, 0.f, 0);
-  // A' = A - T T^T (upper tiles)
-  gemm(s, (int)n1, (int)n1, (int)n2, T, d, 0, MASK_NONE, T, d, 1, MASK_NONE, A, d, -1.f, 1.f, 1);
+  launch_gemm_f32(gemm_args((int)n1, (int)n2, (int)n2, B, d, 0, MASK_NONE, C, d, 1, MASK_LOWER, T, d, 1.f, 0.f, 0), s);
+  // A' = A - T T^T (upper tiles)  and  X^T = U22^T T^T (op(A) = U22^T: keep m >= k)
+  launch_gemm_f32_pair(
+      gemm_args((int)n1, (int)n1, (int)n2, T, d, 0, MASK_NONE, T, d, 1, MASK_NONE, A, d, -1.f, 1.f, 1),
+      gemm_args((int)n2, (int)n1, (int)n2, C, d, 1, MASK_LOWER, T, d, 1, MASK_NONE, Xt, d, 1.f, 0.f, 0), s);
   factor_rec(H, Wk, d, o, n1, info, s);
-  // B <- U11 * T   (U11 upper: keep k >= m)
-  gemm(s, (int)n1, (int)n2, (int)n1, A, d, 0, MASK_UPPER, T, d, 0, MASK_NONE, B, d, 1.f, 0.f, 0);
-  // T <- -B * U22  (U22 upper: keep n >= k)
-  gemm(s, (int)n1, (int)n2, (int)n2, B, d, 0, MASK_NONE, C, d, 0, MASK_UPPER, T, d, -1.f, 0.f, 0);
-  const int64_t cnt = n1 * n2;
-  hipLaunchKernelGGL(copy_block_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
-                     (const float*)T, B, d, (int)n1, (int)n2);
+  // U12 = -U11 X  (U11 upper: keep k >= m; op(B) = X, stored as X^T -> b_trans)
+  launch_gemm_f32(gemm_args((int)n1, (int)n2, (int)n1, A, d, 0, MASK_UPPER, Xt, d, 1, MASK_NONE, B, d, -1.f, 0.f, 0), s);
 }
 
 }  // namespace

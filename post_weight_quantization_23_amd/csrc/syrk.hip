@@ -7,20 +7,21 @@
 // fp32 and the sums are fp32 (v_mfma_f32_32x32x16_{bf16,f16}).
 //
 // Work split: 256 x 256 output tiles of the upper triangle, times `splits`
-// contiguous token ranges.  Each workgroup (8 waves, each a 128 x 64 block of
-// the tile as 4 x 2 MFMA blocks) streams its token range in K-steps of 64.
-// A K-step of X arrives feature-contiguous; each thread loads an 8-token x
-// 8-feature patch (eight 16-byte loads), transposes it in registers with
-// v_perm_b32, and writes eight 16-byte token-contiguous rows into LDS, so
-// every MFMA operand is a single 16-byte LDS read.  The loads run two K-steps
-// ahead and the transposes of the next step are interleaved with the first
-// MFMAs of the current one.  LDS rows are 128 bytes
-// (64 tokens) with the 16-byte chunks XOR-swizzled by the row index, which
-// keeps both the transposed writes and the MFMA reads free of bank conflicts.
-// With one split the tile is added straight into H; otherwise partial tiles
-// go to the workspace and the last workgroup of each tile to finish (an
-// integer arrival counter) sums them in split order -- deterministic, no
-// floating-point atomics -- and adds 2x the sum into H.
+// contiguous token ranges.  Each workgroup (4 waves, each a 128 x 128 block of
+// the tile as 4 x 4 MFMA blocks, accumulators in AGPRs) streams its token range
+// in K-steps of 64.  A K-step of X arrives feature-contiguous; each thread loads
+// an 8-token x 8-feature patch of each slab (eight 16-byte buffer loads),
+// transposes it in registers with v_perm_b32, and writes eight 16-byte
+// token-contiguous rows into LDS, so every MFMA operand is a single 16-byte LDS
+// read.  The loads run two K-steps ahead.  LDS rows are 128 bytes (64 tokens)
+// with the 16-byte chunks XOR-swizzled by the row index, which keeps both the
+// transposed writes and the MFMA reads free of bank conflicts.
+// With one split the tile is added straight into H; otherwise each workgroup
+// writes its partial tile to the workspace and a second kernel sums the
+// partials of every tile in split order (deterministic, no floating-point
+// atomics) and adds twice the sum into H.  Consecutive workgroups take
+// consecutive tiles of the same token range, so the eight XCDs stream the same
+// rows of X at the same time and share them in the memory-side cache.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -34,7 +35,6 @@ constexpr int ROWB = KSTEP * 2;  // bytes per LDS row (64 x 16-bit)
 
 GPTQ_DEV int swz(int f) { return (f ^ (f >> 3)) & 7; }
 
-constexpr int NXCD = 8;   // MI355X: 8 XCDs, workgroups dispatched round-robin
 constexpr int SUPER = 4;  // tiles per super-tile edge in the compact tile order
 
 // The t-th upper-triangle tile (bi <= bj) in super-tile order: super-tiles of
@@ -63,18 +63,6 @@ GPTQ_DEV void tile_coords(int t, int nt, int& bi, int& bj) {
     }
   }
   bi = bj = 0;  // not reached for t < tiles
-}
-
-// Workgroup w runs on XCD w % NXCD.  Give each XCD one contiguous run of the
-// (split-major, compact tile order) work list, so the workgroups one XCD runs
-// at the same time read the same token range of the same feature slabs and
-// share them in that XCD's L2.  Returns false for padding workgroups.
-GPTQ_DEV bool work_unit(int w, int tiles, int splits, int per_xcd, int& tile, int& split) {
-  const int v = (w % NXCD) * per_xcd + w / NXCD;
-  if (w / NXCD >= per_xcd || v >= tiles * splits) return false;
-  split = v / tiles;
-  tile = v % tiles;
-  return true;
 }
 
 // Load the 8 x 8 patch (tokens t0..t0+7, features f0..f0+7) as eight rows of
@@ -245,13 +233,11 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
                                                          int64_t n_tok, int d, int nt,
                                                          int64_t chunk, float* __restrict__ H,
                                                          float* __restrict__ part, int tiles,
-                                                         int splits, int* __restrict__ counters,
-                                                         int per_xcd) {
+                                                         int splits) {
   // LDS: A buffers 0/1 then B buffers 0/1, TILE rows of ROWB bytes each.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  int tile, split;
-  if (!work_unit(blockIdx.x, tiles, splits, per_xcd, tile, split)) return;
+  const int split = (int)blockIdx.x / tiles, tile = (int)blockIdx.x % tiles;
   int bi, bj;
   tile_coords(tile, nt, bi, bj);
   const bool diag = bi == bj;
@@ -314,37 +300,39 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
           pt[r * TILE + c] = compute ? acc[i][j][v] : 0.f;
         }
       }
-    // The last of the tile's `splits` workgroups to finish sums all partials
-    // in split order (deterministic) and adds twice the sum into H.
-    __shared__ int last;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last = (atomicAdd(&counters[tile], 1) == splits - 1);
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const float* p0 = part + (int64_t)tile * (TILE * TILE);
-    for (int e4 = tid; e4 < TILE * TILE / 4; e4 += 256) {
-      const int r = e4 / (TILE / 4), c = (e4 % (TILE / 4)) * 4;
-      floatx4 sum = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < splits; ++k)
-        sum += __builtin_nontemporal_load(
-            reinterpret_cast<const floatx4*>(p0 + (int64_t)k * tiles * (TILE * TILE) + r * TILE + c));
-      const int gi = fi0 + r, gj = fj0 + c;
-      if (gi < d) {
-        float* hp = H + (int64_t)gi * d + gj;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (gj + q < d) hp[q] = __builtin_fmaf(2.0f, sum[q], hp[q]);
-      }
-    }
-    if (tid == 0) counters[tile] = 0;
   }
 }
 
-__global__ void zero_counters_kernel(int* counters, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) counters[i] = 0;
+// H[i][j] += 2 * sum over splits of the partial tiles, in split order.  One
+// thread per 4 consecutive columns of a tile row; the partial loads are
+// issued together before any is summed.
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ part, float* H, int d,
+                                                              int nt, int tiles, int splits) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index over all tiles
+  constexpr int Q = TILE * TILE / 4;
+  if (q >= (int64_t)tiles * Q) return;
+  const int tile = (int)(q / Q), e4 = (int)(q % Q);
+  int bi, bj;
+  tile_coords(tile, nt, bi, bj);
+  const int r = e4 / (TILE / 4), c = (e4 % (TILE / 4)) * 4;
+  const int gi = bi * TILE + r, gj = bj * TILE + c;
+  if (gi >= d || gj >= d) return;
+  const floatx4* p0 = reinterpret_cast<const floatx4*>(part + (int64_t)tile * (TILE * TILE)) + e4;
+  const int64_t stride = (int64_t)tiles * Q;   // one split's partials, in float4
+  floatx4 sum = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 8 <= splits; k += 8) {
+    floatx4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p0 + (k + u) * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; k < splits; ++k) sum += __builtin_nontemporal_load(p0 + k * stride);
+  float* hp = H + (int64_t)gi * d + gj;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    if (gj + u < d) hp[u] = __builtin_fmaf(2.0f, sum[u], hp[u]);
 }
 
 }  // namespace
@@ -378,8 +366,8 @@ SyrkPlan plan_syrk(int64_t d, int64_t n_tok) {
 
 size_t syrk_workspace_bytes(const SyrkPlan& p) {
   if (p.splits <= 1) return 0;
-  // partial tiles, then one arrival counter per tile
-  return (size_t)p.splits * (size_t)p.tiles * TILE * TILE * sizeof(float) + (size_t)p.tiles * sizeof(int);
+  // partial tiles
+  return (size_t)p.splits * (size_t)p.tiles * TILE * TILE * sizeof(float);
 }
 
 void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok, int64_t ldx,
@@ -394,26 +382,24 @@ void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok,
     (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     attr_set = true;
   }
-  const int units = p.tiles * p.splits;
-  const int per_xcd = (units + NXCD - 1) / NXCD;
-  dim3 grid((unsigned)(per_xcd * NXCD));
+  dim3 grid((unsigned)(p.tiles * p.splits));
   float* part = p.splits > 1 ? ws : nullptr;
-  int* counters = nullptr;
-  if (p.splits > 1) {
-    counters = reinterpret_cast<int*>(ws + (size_t)p.splits * p.tiles * TILE * TILE);
-    hipLaunchKernelGGL(zero_counters_kernel, dim3((p.tiles + 255) / 256), dim3(256), 0, s, counters, p.tiles);
-  }
   const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
   const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
 #define GPTQ_SYRK_LAUNCH(DT, V)                                                                        \
   hipLaunchKernelGGL((syrk16_kernel<DT, V>), grid, dim3(256), shmem, s, Xh, ldx, n_tok, (int)d, nt, \
-                     p.chunk, H, part, p.tiles, p.splits, counters, per_xcd)
+                     p.chunk, H, part, p.tiles, p.splits)
   if (dtype == 1) {
     if (vec) GPTQ_SYRK_LAUNCH(1, true); else GPTQ_SYRK_LAUNCH(1, false);
   } else {
     if (vec) GPTQ_SYRK_LAUNCH(2, true); else GPTQ_SYRK_LAUNCH(2, false);
   }
 #undef GPTQ_SYRK_LAUNCH
+  if (p.splits > 1) {
+    const int64_t n4 = (int64_t)p.tiles * (TILE * TILE / 4);
+    hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       (const float*)part, H, (int)d, nt, p.tiles, p.splits);
+  }
 }
 
 }  // namespace gptq
