@@ -21,6 +21,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace gptq {
 
 namespace {
@@ -230,6 +232,95 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmPair pr) {
     }
 }
 
+// Small products (few 64 x 64 tiles, K <= 512): 32 x 32 output tiles, the
+// workgroup's 4 waves split K four ways and load all their operands straight
+// into registers at once (one memory latency instead of one per K-step), then
+// the four partial tiles are summed through LDS in wave order.
+//
+// v_mfma_f32_32x32x2_f32 takes A[m][k0], B[k0][n] from lanes 0..31 and
+// A[m][k1], B[k1][n] from lanes 32..63 for one pair (k0, k1) per step; the sum
+// over k does not depend on which k values share a step, so the wave's K range
+// is split into two contiguous halves (lanes 0..31 the first, 32..63 the
+// second), which makes each lane's values of a row-contiguous operand
+// contiguous in memory.
+constexpr int SK_MAX = 64;   // values per lane per operand (K <= 512)
+
+GPTQ_DEV float ld_a(const GemmArgs& g, int m, int k) {
+  if (m >= g.M || k >= g.K || !keep_a(g.a_mask, g.a_off, m, k)) return 0.f;
+  return g.a_trans ? g.A[(int64_t)k * g.lda + m] : g.A[(int64_t)m * g.lda + k];
+}
+GPTQ_DEV float ld_b(const GemmArgs& g, int k, int n) {
+  if (n >= g.N || k >= g.K || !keep_b(g.b_mask, g.b_off, k, n)) return 0.f;
+  return g.b_trans ? g.B[(int64_t)n * g.ldb + k] : g.B[(int64_t)k * g.ldb + n];
+}
+
+__global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmPair pr) {
+  const bool second = (int)blockIdx.x >= pr.tiles0;
+  const GemmArgs& g = second ? pr.g[1] : pr.g[0];
+  const int bid = second ? (int)blockIdx.x - pr.tiles0 : (int)blockIdx.x;
+  const int tiles_n = (g.N + 31) / 32;
+  const int m0 = (bid / tiles_n) * 32, n0 = (bid % tiles_n) * 32;
+  if (g.upper_only && n0 + 32 <= m0) return;
+  __shared__ floatx16 red[3][64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 31, h = lane >> 5;
+  // K range of this wave: [kw, kw + kq), half h: [kh, kh + kq/2); kq % 8 == 0
+  const int kq = (((g.K + 3) / 4) + 7) / 8 * 8;
+  const int half = kq / 2;
+  const int kh = wave * kq + h * half;
+  const int m = m0 + li, n = n0 + li;
+
+  float a[SK_MAX], b[SK_MAX];
+  const bool a_vec = !g.a_trans && ((g.lda & 3) == 0) && ((reinterpret_cast<uintptr_t>(g.A) & 15) == 0);
+  const bool b_vec = g.b_trans && ((g.ldb & 3) == 0) && ((reinterpret_cast<uintptr_t>(g.B) & 15) == 0);
+#pragma unroll
+  for (int s = 0; s < SK_MAX; s += 4) {
+    if (s < half) {
+      const int k = kh + s;
+      if (a_vec && m < g.M && k + 3 < g.K) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(g.A + (int64_t)m * g.lda + k);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a[s + c] = keep_a(g.a_mask, g.a_off, m, k + c) ? v[c] : 0.f;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a[s + c] = ld_a(g, m, k + c);
+      }
+      if (b_vec && n < g.N && k + 3 < g.K) {
+        const floatx4 v = *reinterpret_cast<const floatx4*>(g.B + (int64_t)n * g.ldb + k);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[s + c] = keep_b(g.b_mask, g.b_off, k + c, n) ? v[c] : 0.f;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[s + c] = ld_b(g, k + c, n);
+      }
+    }
+  }
+  floatx16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+  for (int s = 0; s < SK_MAX; ++s)
+    if (s < half) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+
+  if (wave > 0) red[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) acc += red[w][lane];
+  // lane holds D[8*(v/4) + 4*h + v%4][li]
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = m0 + 8 * (v >> 2) + 4 * h + (v & 3);
+    if (row < g.M && n < g.N) {
+      float* p = g.C + (int64_t)row * g.ldc + n;
+      float out = g.alpha * acc[v];
+      if (g.beta != 0.f) out = __builtin_fmaf(g.beta, *p, out);
+      *p = out;
+    }
+  }
+}
+
 template <int TM, int TN, int KT>
 int64_t tiles_of(const GemmArgs& g) {
   return (g.M <= 0 || g.N <= 0) ? 0 : (int64_t)((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
@@ -255,8 +346,22 @@ void launch_tile(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
 }
 
 void launch_dispatch(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
-  // 128 x 128 tiles when that already gives enough workgroups, else 64 x 64.
+  // 128 x 128 tiles when that already gives enough workgroups, else 64 x 64;
+  // problems too small to fill the chip with 64 x 64 tiles (and K <= 512) go
+  // to the small-product kernel.
   const int64_t t128 = tiles_of<128, 128, 32>(g0) + (g1 ? tiles_of<128, 128, 32>(*g1) : 0);
+  const int64_t t64 = tiles_of<64, 64, 32>(g0) + (g1 ? tiles_of<64, 64, 32>(*g1) : 0);
+  const int kmax = std::max(g0.K, g1 ? g1->K : 0);
+  if (t64 < 256 && kmax <= 8 * SK_MAX) {
+    GemmPair pr;
+    pr.g[0] = g0;
+    pr.g[1] = g1 ? *g1 : g0;
+    const int64_t t0 = tiles_of<32, 32, 32>(g0);
+    const int64_t t1 = g1 ? tiles_of<32, 32, 32>(*g1) : 0;
+    pr.tiles0 = (int)t0;
+    if (t0 + t1 > 0) hipLaunchKernelGGL(gemm_f32_small_kernel, dim3((unsigned)(t0 + t1)), dim3(256), 0, s, pr);
+    return;
+  }
   if (t128 >= 480) {
     launch_tile<128, 128, 32>(g0, g1, s);
   } else {
