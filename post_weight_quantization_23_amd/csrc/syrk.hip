@@ -129,12 +129,12 @@ GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_
   // Loader role: every thread carries one 8-token x 8-feature patch of the
   // row slab (A) and one of the column slab (B, not needed on diagonal tiles).
   const int tb = tid >> 5, fb = tid & 31;
-  u32x4 ra[8], rb[8];
+  u32x4 ra0[8], rb0[8];
   const int64_t nsteps = (t_end - t_beg + KSTEP - 1) / KSTEP;
   // byte offset of the thread's patch inside a token row
   const int off_a = 2 * (fi0 + fb * 8), off_b = 2 * (fj0 + fb * 8);
 
-  auto fetch = [&](int64_t st) {
+  auto fetch = [&](int64_t st, u32x4 (&ra)[8], u32x4 (&rb)[8]) {
     const int64_t t0 = t_beg + st * KSTEP + tb * 8;
     if constexpr (FAST) {
       // One descriptor per K-step (wave-uniform): base at the step's first
@@ -167,9 +167,13 @@ GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_
       *reinterpret_cast<u32x4*>(lds + f * ROWB + ((tb ^ swz(f)) * 16)) = o;
     }
   };
-  auto stage_half = [&](int buf, int m0) {
-    stage4(a_buf(buf), ra, m0);
-    if (!diag) stage4(b_buf(buf), rb, m0);
+  auto stage = [&](int buf, const u32x4 (&ra)[8], const u32x4 (&rb)[8]) {
+    stage4(a_buf(buf), ra, 0);
+    stage4(a_buf(buf), ra, 4);
+    if (!diag) {
+      stage4(b_buf(buf), rb, 0);
+      stage4(b_buf(buf), rb, 4);
+    }
   };
   u32x4 fa[2][4], fbm[2][4];
   auto frags = [&](const unsigned char* as, const unsigned char* bs, int kk, u32x4 (&a)[4], u32x4 (&b)[4]) {
@@ -191,40 +195,57 @@ GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<DT>(a[i], b[j], acc[i][j]);
   };
+  // K-step st from LDS buffer buf; (na, nb) hold the raw patches of step
+  // st+1: they are transposed into the other buffer and then refilled with
+  // the loads of step st+2.
+  auto step = [&](int64_t st, int buf, u32x4 (&na)[8], u32x4 (&nb)[8]) {
+    const unsigned char* as = a_buf(buf);
+    const unsigned char* bs = diag ? a_buf(buf) : b_buf(buf);
+    if (compute) {
+      frags(as, bs, 0, fa[0], fbm[0]);
+      frags(as, bs, 1, fa[1], fbm[1]);
+    }
+    if (st + 1 < nsteps) stage(buf ^ 1, na, nb);
+    if (st + 2 < nsteps) fetch(st + 2, na, nb);
+    if (compute) {
+      mfmas(fa[0], fbm[0]);
+      frags(as, bs, 2, fa[0], fbm[0]);
+      mfmas(fa[1], fbm[1]);
+      frags(as, bs, 3, fa[1], fbm[1]);
+      mfmas(fa[0], fbm[0]);
+      mfmas(fa[1], fbm[1]);
+    }
+    __syncthreads();
+  };
+  // The same step without branches (st + 2 < nsteps, every wave computes), so
+  // that the transposes, LDS writes and loads share one scheduling region with
+  // the MFMAs.
+  auto steady = [&](int64_t st, int buf, u32x4 (&na)[8], u32x4 (&nb)[8]) {
+    const unsigned char* as = a_buf(buf);
+    const unsigned char* bs = diag ? a_buf(buf) : b_buf(buf);
+    frags(as, bs, 0, fa[0], fbm[0]);
+    frags(as, bs, 1, fa[1], fbm[1]);
+    stage(buf ^ 1, na, nb);
+    fetch(st + 2, na, nb);
+    mfmas(fa[0], fbm[0]);
+    frags(as, bs, 2, fa[0], fbm[0]);
+    mfmas(fa[1], fbm[1]);
+    frags(as, bs, 3, fa[1], fbm[1]);
+    mfmas(fa[0], fbm[0]);
+    mfmas(fa[1], fbm[1]);
+    __syncthreads();
+  };
 
   if (nsteps > 0) {
-    fetch(0);
-    stage_half(0, 0);
-    stage_half(0, 4);
-    if (nsteps > 1) fetch(1);
+    fetch(0, ra0, rb0);
+    stage(0, ra0, rb0);
+    if (nsteps > 1) fetch(1, ra0, rb0);
     __syncthreads();
-    int buf = 0;
-    for (int64_t st = 0; st < nsteps; ++st) {
-      const bool stage_next = st + 1 < nsteps;
-      const unsigned char* as = a_buf(buf);
-      const unsigned char* bs = diag ? a_buf(buf) : b_buf(buf);
-      if (compute) {
-        frags(as, bs, 0, fa[0], fbm[0]);
-        frags(as, bs, 1, fa[1], fbm[1]);
-      }
-      // Transpose step st+1 into the other buffer and issue the loads of
-      // step st+2 first, so that they have a whole step to arrive.
-      if (stage_next) {
-        stage_half(buf ^ 1, 0);
-        stage_half(buf ^ 1, 4);
-      }
-      if (st + 2 < nsteps) fetch(st + 2);
-      if (compute) {
-        mfmas(fa[0], fbm[0]);
-        frags(as, bs, 2, fa[0], fbm[0]);
-        mfmas(fa[1], fbm[1]);
-        frags(as, bs, 3, fa[1], fbm[1]);
-        mfmas(fa[0], fbm[0]);
-        mfmas(fa[1], fbm[1]);
-      }
-      __syncthreads();
-      buf ^= 1;
+    int64_t st = 0;
+    if constexpr (FAST && !DIAG) {
+      for (; st + 2 < nsteps; ++st) steady(st, (int)(st & 1), ra0, rb0);
     }
+    for (; st < nsteps; ++st) step(st, (int)(st & 1), ra0, rb0);
   }
 }
 
