@@ -127,6 +127,13 @@ gptq_status gptq_prepare(float* H_to_U, int64_t d, float percdamp, int act_order
  * perm     : int32[c] from gptq_prepare, or NULL for the identity order.
  * dead     : uint8[c] from gptq_prepare (original order), or NULL (none).
  * bits     : 2, 3, 4 or 8.
+ * sym      : 0 -> asymmetric ruler (range stretched to include 0, zero =
+ *            rne(-min / scale)); 1 -> symmetric ruler: range [-m, m] with
+ *            m = max(|min|, |max|), scale = 2m / (2^bits - 1), zero = the
+ *            middle tick 2^(bits-1).  The pages name a symmetric option
+ *            ("Paper vs. code") without a formula; this is the plainest
+ *            reading that keeps 0.0 exactly on a tick.  Other values:
+ *            GPTQ_EINVAL.
  * groupsize: <= 0 -> one ruler per row, fitted on the original weights
  *            before dead inputs are zeroed; > 0 -> one ruler per run of
  *            `groupsize` columns in processing order, fitted when the loop
@@ -151,7 +158,7 @@ gptq_status gptq_quantize_layer_workspace_size(int64_t r, int64_t c, int64_t blo
                                                size_t* bytes);
 gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t c,
                                 int64_t ldw, const float* U, const int32_t* perm,
-                                const uint8_t* dead, int bits, int64_t groupsize,
+                                const uint8_t* dead, int bits, int sym, int64_t groupsize,
                                 int64_t blocksize, uint8_t* codes, float* scales,
                                 int32_t* zeros, int32_t* g_idx, float* W_hat,
                                 float* row_loss, void* ws, size_t ws_bytes, void* stream);

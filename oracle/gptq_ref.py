@@ -44,6 +44,8 @@ Readings where the pages are silent (each is also listed in the design doc):
 * Ties round half to even, for the code and for the zero point; the code is
   rne(w/scale) + zero, then clamped to [0, 2^b - 1].  An all-zero range uses
   [-1, 1].
+* The symmetric ruler (an option the page names without a formula) uses the
+  range [-m, m], m = max|w|, and the middle tick 2^(b-1) as its zero point.
 * Precision of decisions: the page's code runs in full fp32, so every step that
   turns floating point into an integer -- the ruler (min, max, scale, zero)
   and the division w/scale that picks a tick -- is evaluated in IEEE fp32 here
@@ -111,8 +113,15 @@ def hessian(X, chunk: int = 1 << 15) -> np.ndarray:
 # (or group), the range stretched to include 0, the zero point rounded to a
 # whole tick, w_hat = scale * (q - zero).
 # ---------------------------------------------------------------------------
-def fit_ruler(w, bits: int):
-    """Fit one asymmetric min-max ruler per row of `w` ([rows, k], k >= 1).
+def fit_ruler(w, bits: int, sym: bool = False):
+    """Fit one min-max ruler per row of `w` ([rows, k], k >= 1).
+
+    Asymmetric (the default): the range [min, max] stretched to include 0,
+    scale = (max - min) / (2^b - 1), zero = rne(-min / scale).
+    Symmetric (the pages name the option without a formula; plainest reading):
+    the range [-m, m] with m = max(|min|, |max|), scale = 2m / (2^b - 1), and
+    the zero point the middle tick 2^(b-1), so 0.0 stays exactly on a tick.
+    An all-zero range uses [-1, 1] in both modes.
 
     Returns (scale fp32 [rows], zero float [rows] holding whole numbers,
     zero_unrounded fp32 [rows]).  Evaluated in fp32 (see module docstring).
@@ -122,12 +131,18 @@ def fit_ruler(w, bits: int):
         raise ValueError("fit_ruler needs a non-empty [rows, k] array")
     xmin = np.minimum(w32.min(axis=1), F32(0.0))
     xmax = np.maximum(w32.max(axis=1), F32(0.0))
+    if sym:
+        m = np.maximum(-xmin, xmax).astype(F32)
+        xmin, xmax = (-m).astype(F32), m
     flat = (xmin == 0) & (xmax == 0)
     xmin = np.where(flat, F32(-1.0), xmin).astype(F32)
     xmax = np.where(flat, F32(1.0), xmax).astype(F32)
     maxq = F32(2 ** bits - 1)
     scale = ((xmax - xmin) / maxq).astype(F32)
-    zero_t = (-xmin / scale).astype(F32)
+    if sym:
+        zero_t = np.full(scale.shape, F32(2 ** (bits - 1)), F32)
+    else:
+        zero_t = (-xmin / scale).astype(F32)
     zero = np.rint(zero_t).astype(F64)
     return scale, zero, zero_t
 
@@ -247,7 +262,7 @@ class TieReplay:
 
 def gptq_quantize(W0, H_raw, bits: int, groupsize: int = -1, percdamp: float = 0.01,
                   act_order: bool = False, blocksize: int | None = None,
-                  U=None, replay: TieReplay | None = None, rows=None):
+                  U=None, replay: TieReplay | None = None, rows=None, sym: bool = False):
     """Quantize one linear layer with GPTQ.
 
     W0 [r, c] holds one output per row and one input per column.  H_raw is the
@@ -258,6 +273,7 @@ def gptq_quantize(W0, H_raw, bits: int, groupsize: int = -1, percdamp: float = 0
     upper factor to use (processing order) instead of computing one -- the
     dead-input set and the permutation are still derived from H_raw.
     `rows` (indices into the full layer) is only used to index `replay`.
+    `sym` selects the symmetric ruler (see fit_ruler).
 
     Returns a dict: codes [r, c] (original column order), scales and zeros
     [r, n_groups] (group order = processing order), g_idx [c], w_hat [r, c],
@@ -272,7 +288,7 @@ def gptq_quantize(W0, H_raw, bits: int, groupsize: int = -1, percdamp: float = 0
 
     # Per-row ruler, fitted on the original weights before anything else.
     if groupsize <= 0:
-        row_scale, row_zero, row_zt = fit_ruler(W0, bits) if c else (None, None, None)
+        row_scale, row_zero, row_zt = fit_ruler(W0, bits, sym) if c else (None, None, None)
         if replay is not None and c:
             row_zero = replay.zero(rows, 0, row_zero, row_zt)
 
@@ -305,7 +321,7 @@ def gptq_quantize(W0, H_raw, bits: int, groupsize: int = -1, percdamp: float = 0
         for j in range(i1, i2):
             if groupsize > 0 and j % groupsize == 0:
                 g = j // groupsize
-                scale, zero, zt = fit_ruler(W[:, j:j + groupsize], bits)
+                scale, zero, zt = fit_ruler(W[:, j:j + groupsize], bits, sym)
                 if replay is not None:
                     zero = replay.zero(rows, g, zero, zt)
                 scales[:, g] = scale
@@ -348,7 +364,7 @@ def gptq_quantize(W0, H_raw, bits: int, groupsize: int = -1, percdamp: float = 0
 # snapped to its nearest tick independently, no repair.  Written separately
 # from gptq_quantize on purpose (it pins it).
 # ---------------------------------------------------------------------------
-def rtn(W, bits: int, groupsize: int = -1):
+def rtn(W, bits: int, groupsize: int = -1, sym: bool = False):
     """Plain round-to-nearest on per-row (groupsize <= 0) or per-group rulers.
 
     Returns (codes int64 [r, c], w_hat float64 [r, c]).
@@ -359,7 +375,7 @@ def rtn(W, bits: int, groupsize: int = -1):
     w_hat = np.zeros((r, c), F64)
     spans = [(0, c)] if groupsize <= 0 else [(s, min(s + groupsize, c)) for s in range(0, c, groupsize)]
     for a, b in spans:
-        scale, zero, _ = fit_ruler(W[:, a:b], bits)
+        scale, zero, _ = fit_ruler(W[:, a:b], bits, sym)
         for j in range(a, b):
             q, _ = round_to_grid(W[:, j], scale, zero, bits)
             codes[:, j] = q.astype(np.int64)

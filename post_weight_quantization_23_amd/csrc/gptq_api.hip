@@ -151,13 +151,14 @@ gptq_status gptq_quantize_layer_workspace_size(int64_t r, int64_t c, int64_t blo
 
 gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t c, int64_t ldw,
                                 const float* U, const int32_t* perm, const uint8_t* dead, int bits,
-                                int64_t groupsize, int64_t blocksize, uint8_t* codes, float* scales,
+                                int sym, int64_t groupsize, int64_t blocksize, uint8_t* codes, float* scales,
                                 int32_t* zeros, int32_t* g_idx, float* W_hat, float* row_loss, void* ws,
                                 size_t ws_bytes, void* stream) {
   const char* fn = "gptq_quantize_layer";
   if (r < 0 || c < 0) return fail(GPTQ_EINVAL, fn, "negative size");
   if (!valid_dtype(wt)) return fail(GPTQ_EDTYPE, fn, "wt must be GPTQ_F32, GPTQ_BF16 or GPTQ_F16");
   if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return fail(GPTQ_EUNSUPPORTED, fn, "bits must be 2, 3, 4 or 8");
+  if (sym != 0 && sym != 1) return fail(GPTQ_EINVAL, fn, "sym must be 0 or 1");
   if (blocksize < 1 || blocksize > 128) return fail(GPTQ_EUNSUPPORTED, fn, "blocksize must be 1..128");
   if (groupsize > 0 && (groupsize % blocksize) != 0 && (blocksize % groupsize) != 0)
     return fail(GPTQ_EUNSUPPORTED, fn, "groupsize must be a multiple or a divisor of blocksize");
@@ -174,7 +175,7 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t
   if (!aligned(ws, 256)) return fail(GPTQ_EALIGN, fn, "workspace not 256-byte aligned");
   gptq::QuantArgs a;
   a.W = W; a.wt = (int)wt; a.r = r; a.c = c; a.ldw = ldw; a.U = U; a.perm = perm; a.dead = dead;
-  a.bits = bits; a.groupsize = groupsize; a.blocksize = blocksize; a.codes = codes; a.scales = scales;
+  a.bits = bits; a.sym = sym; a.groupsize = groupsize; a.blocksize = blocksize; a.codes = codes; a.scales = scales;
   a.zeros = zeros; a.g_idx = g_idx; a.W_hat = W_hat; a.row_loss = row_loss; a.ws = ws;
   gptq::launch_quantize(a, reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);

@@ -55,6 +55,7 @@ struct QuantArgs {
   const int32_t* perm;
   const uint8_t* dead;
   int bits;
+  int sym;  // symmetric ruler
   int64_t groupsize, blocksize;
   uint8_t* codes;
   float* scales;

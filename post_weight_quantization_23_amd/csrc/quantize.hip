@@ -39,17 +39,24 @@ namespace {
 
 constexpr int BMAX = 128;
 
-// Asymmetric min-max ruler ("What quantization is"): range stretched to
-// include 0, scale = (max - min) / (2^b - 1), zero = rne(-min / scale); an
-// all-zero range uses [-1, 1].  IEEE fp32 throughout.
-GPTQ_DEV void fit_ruler(float mn, float mx, float maxq, float& scale, float& zero) {
+// Min-max ruler ("What quantization is"), IEEE fp32 throughout.  Asymmetric:
+// the range stretched to include 0, scale = (max - min) / (2^b - 1), zero =
+// rne(-min / scale).  Symmetric: the range [-m, m], m = max(|min|, |max|),
+// scale = 2m / (2^b - 1), zero = the middle tick (maxq + 1) / 2.  An all-zero
+// range uses [-1, 1].
+GPTQ_DEV void fit_ruler(float mn, float mx, float maxq, bool sym, float& scale, float& zero) {
   float lo = fminf(mn, 0.f), hi = fmaxf(mx, 0.f);
+  if (sym) {
+    const float m = fmaxf(-lo, hi);
+    lo = -m;
+    hi = m;
+  }
   if (lo == 0.f && hi == 0.f) {
     lo = -1.f;
     hi = 1.f;
   }
   scale = __fdiv_rn(hi - lo, maxq);
-  zero = rne(__fdiv_rn(-lo, scale));
+  zero = sym ? 0.5f * (maxq + 1.f) : rne(__fdiv_rn(-lo, scale));
 }
 
 // perm comes from device memory; an index outside [0, c) (a caller bug) is
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp) {
     }
     if (threadIdx.x == 0) {
       float scale, zero;
-      fit_ruler(smn[0], smx[0], (float)((1 << a.bits) - 1), scale, zero);
+      fit_ruler(smn[0], smx[0], (float)((1 << a.bits) - 1), a.sym != 0, scale, zero);
       a.scales[row] = scale;
       a.zeros[row] = (int32_t)zero;
     }
@@ -170,6 +177,7 @@ struct BlockArgs {
   int64_t r, c, i1;
   int Bw;
   int bits;
+  int sym;
   int64_t groupsize;
   const int32_t* perm;
   uint8_t* codes;
@@ -186,7 +194,7 @@ struct BlockArgs {
 // copy for the part beyond it).
 template <int L, int S>
 GPTQ_DEV void fit_group(const float (&w)[S], int p, int j, int Bw, int64_t g, int64_t i1, int64_t c,
-                        const float* Wrow, bool valid, float maxq, float& scale, float& zero) {
+                        const float* Wrow, bool valid, float maxq, bool sym, float& scale, float& zero) {
   const int64_t gend = min(i1 + j + g, c);
   float mn = __builtin_inff(), mx = -__builtin_inff();
 #pragma unroll
@@ -206,7 +214,7 @@ GPTQ_DEV void fit_group(const float (&w)[S], int p, int j, int Bw, int64_t g, in
   }
   mn = row_min<L>(mn);
   mx = row_max<L>(mx);
-  fit_ruler(mn, mx, maxq, scale, zero);
+  fit_ruler(mn, mx, maxq, sym, scale, zero);
 }
 
 // Stage V[j][k] = U[i1 + j][i1 + k] / U[i1 + j][i1 + j] for k > j (0 on and
@@ -286,7 +294,7 @@ GPTQ_DEV void block_ruler(const BlockArgs& a, const float (&w)[S], int p, int64_
       zero = (float)a.zeros[row * a.n_groups];
     }
   } else if (i1 % g == 0) {
-    fit_group<L, S>(w, p, 0, Bw, g, i1, a.c, Wrow, valid, maxq, scale, zero);
+    fit_group<L, S>(w, p, 0, Bw, g, i1, a.c, Wrow, valid, maxq, a.sym != 0, scale, zero);
     if (valid && p == 0) {
       a.scales[row * a.n_groups + i1 / g] = scale;
       a.zeros[row * a.n_groups + i1 / g] = (int32_t)zero;
@@ -346,7 +354,7 @@ GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row,
     const int mj = j / L, pj = j % L;
     if constexpr (MIDGROUPS) {
       if (j > 0 && j == next_group && (FULL || j < Bw)) {
-        fit_group<L, S>(w, p, j, Bw, g, i1, c, Wrow, valid, maxq, scale, zero);
+        fit_group<L, S>(w, p, j, Bw, g, i1, c, Wrow, valid, maxq, a.sym != 0, scale, zero);
         y = __fdiv_rn(1.0f, scale);
         lo = -zero;
         hi = maxq - zero;
@@ -531,6 +539,7 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   b.r = r;
   b.c = c;
   b.bits = a.bits;
+  b.sym = a.sym;
   b.groupsize = a.groupsize;
   b.perm = a.perm;
   b.codes = a.codes;

@@ -112,12 +112,14 @@ def prepare(H: torch.Tensor, percdamp: float = 0.01, act_order: bool = False, ch
 
 def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor | None, dead: torch.Tensor | None,
                    bits: int = 4, groupsize: int = 128, blocksize: int = 128, want_w_hat: bool = False,
-                   want_loss: bool = True, ws: Workspace | None = None, out: dict | None = None) -> dict:
+                   want_loss: bool = True, ws: Workspace | None = None, out: dict | None = None,
+                   sym: bool = False) -> dict:
     """GPTQ-quantize W [r, c] with the factor U from prepare().
 
     Returns {codes uint8 [r, c], scales fp32 [r, G], zeros int32 [r, G], g_idx int32 [c],
     w_hat fp32 [r, c] or None, row_loss fp32 [r] or None}; outputs are in the
     original column order.  `out` may supply preallocated tensors with those keys.
+    `sym` selects the symmetric ruler (zero point at the middle tick).
     """
     _need(W, "W", None, 2)
     if W.dtype not in _DT:
@@ -148,7 +150,7 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor | None, 
     need = _lib.query("gptq_quantize_layer_workspace_size", r, c, blocksize)
     buf, nb = _ws(ws, need, dev)
     _lib.call("gptq_quantize_layer", _ptr(W), _DT[W.dtype], r, c, W.stride(0), _ptr(U), _ptr(perm), _ptr(dead),
-              int(bits), int(groupsize), int(blocksize), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
+              int(bits), int(bool(sym)), int(groupsize), int(blocksize), _ptr(codes), _ptr(scales), _ptr(zeros), _ptr(g_idx),
               _ptr(w_hat), _ptr(row_loss), _ptr(buf), nb, _stream())
     return {"codes": codes, "scales": scales, "zeros": zeros, "g_idx": g_idx, "w_hat": w_hat,
             "row_loss": row_loss}

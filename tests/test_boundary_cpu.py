@@ -96,11 +96,13 @@ def test_quantize_argument_errors(lib):
     f = "gptq_quantize_layer"
     A = ALIGNED
 
-    def q(W=A, wt=1, r=8, c=256, ldw=256, U=A, bits=4, g=128, B=128, codes=A, ws=A, nws=1 << 30):
-        return _st(lib, f, W, wt, r, c, ldw, U, None, None, bits, g, B, codes, A, A, A, None, None, ws, nws, None)
+    def q(W=A, wt=1, r=8, c=256, ldw=256, U=A, bits=4, g=128, B=128, codes=A, ws=A, nws=1 << 30, sym=0):
+        return _st(lib, f, W, wt, r, c, ldw, U, None, None, bits, sym, g, B, codes, A, A, A, None, None, ws, nws,
+                   None)
 
     assert q(r=0) == 0 and q(c=0) == 0
     assert q(bits=5) == 5 and q(bits=1) == 5
+    assert q(sym=2) == 1 and q(sym=-1) == 1
     assert q(B=0) == 5 and q(B=256) == 5
     assert q(g=96, B=128) == 5            # neither a multiple nor a divisor
     assert q(wt=3) == 2

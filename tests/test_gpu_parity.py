@@ -69,14 +69,16 @@ def full_sym(Hu):
     return Hu + np.triu(Hu, 1).T
 
 
-def stagewise(W_host, H_gpu, bits, groupsize, blocksize, act_order, percdamp=0.01, rows=None, wdtype="float32"):
+def stagewise(W_host, H_gpu, bits, groupsize, blocksize, act_order, percdamp=0.01, rows=None, wdtype="float32",
+              sym=False):
     """GPU prepare + quantize, then the oracle's loop with the GPU's U and tie replay."""
     q = gq()
     Hf = full_sym(H_gpu.double().cpu().numpy())
     U = H_gpu.clone()
     perm, dead, info = q.prepare(U, percdamp=percdamp, act_order=act_order)
     W = to_dev(W_host, DT[wdtype])
-    out = q.quantize_layer(W, U, perm, dead, bits=bits, groupsize=groupsize, blocksize=blocksize, want_w_hat=True)
+    out = q.quantize_layer(W, U, perm, dead, bits=bits, groupsize=groupsize, blocksize=blocksize, want_w_hat=True,
+                           sym=sym)
     torch.cuda.synchronize()
     Ug = U.double().cpu().numpy()
     permg = perm.cpu().numpy().astype(np.int64)
@@ -94,7 +96,7 @@ def stagewise(W_host, H_gpu, bits, groupsize, blocksize, act_order, percdamp=0.0
     sel = np.arange(W_host.shape[0]) if rows is None else np.asarray(rows)
     rep = ref.TieReplay(codes[sel][:, permg], zeros[sel])
     res = ref.gptq_quantize(W_host[sel].astype(np.float64), Hf, bits, groupsize, percdamp, act_order,
-                            U=Ug, replay=rep)
+                            U=Ug, replay=rep, sym=sym)
     n = len(sel) * W_host.shape[1]
     assert rep.hard == 0 and rep.zero_hard == 0, f"hard mismatches {rep.hard} codes / {rep.zero_hard} zeros"
     assert rep.near_ties <= NEAR_TIE_FRAC * n, f"near ties {rep.near_ties} of {n}"
@@ -197,6 +199,28 @@ def test_quantize_stagewise(r, c, bits, g, B, act, n_dead, wdtype):
     stagewise(W, H, bits, g, B, act, wdtype=wdtype)
 
 
+SYM_CASES = [
+    # r, c, bits, groupsize, blocksize, act_order, n_dead, wdtype
+    (128, 256, 4, -1, 128, False, 0, "float32"),
+    (64, 384, 3, 128, 128, True, 1, "bfloat16"),
+    (1100, 256, 4, 32, 128, False, 0, "bfloat16"),   # 16 lanes per row, groups inside blocks
+    (40, 160, 8, 64, 64, False, 0, "float16"),
+    (50, 256, 2, -1, 128, True, 2, "float32"),
+    (20, 300, 4, 256, 128, False, 0, "float32"),     # group spanning two blocks
+]
+
+
+@pytest.mark.parametrize("r,c,bits,g,B,act,n_dead,wdtype", SYM_CASES)
+def test_quantize_stagewise_symmetric(r, c, bits, g, B, act, n_dead, wdtype):
+    W = S.weights_host(r, c, wid=170 + c, dtype=wdtype)
+    X = S.activations_host(3 * c, c, "t4", outliers=4, gain=20.0, wid=171 + c)
+    if n_dead:
+        X[:, (np.arange(n_dead) * 11 + 3) % c] = 0.0
+    H = gpu_hessian(X, "float32")
+    out, res, _ = stagewise(W, H, bits, g, B, act, wdtype=wdtype, sym=True)
+    assert np.all(out["zeros"].cpu().numpy() == 2 ** (bits - 1))
+
+
 @pytest.mark.parametrize("g", [-1, 32, 128])
 def test_identity_hessian_is_bitwise_rtn(g):
     r, c = 300, 256
@@ -208,6 +232,11 @@ def test_identity_hessian_is_bitwise_rtn(g):
     out = q.quantize_layer(to_dev(W, torch.bfloat16), U, perm, dead, bits=4, groupsize=g, want_w_hat=True)
     torch.cuda.synchronize()
     codes, w_hat = ref.rtn(W.astype(np.float64), 4, g)
+    np.testing.assert_array_equal(out["codes"].cpu().numpy(), codes)
+    np.testing.assert_array_equal(out["w_hat"].cpu().numpy(), w_hat.astype(np.float32))
+    out = q.quantize_layer(to_dev(W, torch.bfloat16), U, perm, dead, bits=3, groupsize=g, want_w_hat=True, sym=True)
+    torch.cuda.synchronize()
+    codes, w_hat = ref.rtn(W.astype(np.float64), 3, g, sym=True)
     np.testing.assert_array_equal(out["codes"].cpu().numpy(), codes)
     np.testing.assert_array_equal(out["w_hat"].cpu().numpy(), w_hat.astype(np.float32))
 

@@ -384,3 +384,59 @@ def test_pack_layout_closed_forms_and_round_trip():
         words = ref.pack_codes(codes, bits)
         assert words.nbytes == 5 * c * bits // 8
         np.testing.assert_array_equal(ref.unpack_codes(words, bits, c), codes)
+
+
+# --- symmetric grid (the pages name the option without a formula; reading:
+# range [-m, m], m = max|w|, scale = 2m/(2^b - 1), zero = the middle tick) ---
+def test_symmetric_grid_closed_form():
+    w = np.array([[-0.8, 0.4, 0.0, 0.05]])
+    scale, zero, zt = ref.fit_ruler(w, 4, sym=True)
+    s32 = np.float32(np.float32(1.6) / np.float32(15.0))     # 2m / 15 in fp32
+    assert scale[0] == s32 and zero[0] == 8.0 and zt[0] == 8.0
+    q, t = ref.round_to_grid(w[0], scale[0], zero[0], 4)
+    # -0.8 / s = -7.5 -> rne -8 -> code 0;  0.4 / s = 3.75 -> 4 -> 12;  0 -> 8
+    np.testing.assert_array_equal(q[:3], [0.0, 12.0, 8.0])
+    assert ref.dequantize(np.float64(8.0), scale[0], 8.0) == 0.0      # 0 exactly on a tick
+    # the asymmetric ruler of the same row differs (the page's example grid)
+    a_scale, a_zero, _ = ref.fit_ruler(w, 4)
+    assert a_zero[0] == 10.0 and a_scale[0] != scale[0]
+
+
+def test_symmetric_grid_is_odd_up_to_the_extra_negative_tick():
+    rng = np.random.default_rng(31)
+    w = rng.standard_normal((6, 50)) * 0.03
+    for bits in (2, 3, 4, 8):
+        s1, z1, _ = ref.fit_ruler(w, bits, sym=True)
+        s2, z2, _ = ref.fit_ruler(-w, bits, sym=True)
+        np.testing.assert_array_equal(s1, s2)
+        np.testing.assert_array_equal(z1, z2)
+        assert np.all(z1 == 2 ** (bits - 1))
+        for i in range(w.shape[0]):
+            q1, t1 = ref.round_to_grid(w[i], s1[i], z1[i], bits)
+            q2, _ = ref.round_to_grid(-w[i], s2[i], z2[i], bits)
+            inner = np.abs(t1) < 2 ** (bits - 1) - 0.5 - 1e-3   # no clamp, no tie
+            np.testing.assert_array_equal(q2[inner], 2 * z1[i] - q1[inner])
+
+
+@pytest.mark.parametrize("groupsize", [-1, 16])
+def test_symmetric_identity_hessian_is_round_to_nearest(groupsize):
+    rng = np.random.default_rng(32)
+    W0 = rng.standard_normal((13, 48)) * 0.02
+    out = ref.gptq_quantize(W0, ref.hessian(2.0 * np.eye(48)), bits=4, groupsize=groupsize, sym=True)
+    codes, w_hat = ref.rtn(W0, 4, groupsize, sym=True)
+    np.testing.assert_array_equal(out["codes"], codes)
+    np.testing.assert_array_equal(out["w_hat"], w_hat)
+    assert np.all(out["zeros"] == 8)
+
+
+def test_symmetric_tiny_layers_against_brute_force():
+    rng = np.random.default_rng(33)
+    for _ in range(20):
+        d = int(rng.integers(3, 6))
+        X = _correlated_x(rng, 24, d, mix=0.8)
+        w0 = rng.standard_normal(d) * 0.1
+        out = ref.gptq_quantize(w0[None], ref.hessian(X), bits=3, sym=True)
+        scale, zero = out["scales"][0, 0], out["zeros"][0, 0]
+        assert zero == 4
+        _, best = ref.brute_force_row(w0, X, scale, zero, 3)
+        assert best <= ref.layer_loss_from_x(w0[None], out["w_hat"], X) * (1 + 1e-12)
