@@ -79,6 +79,7 @@ __all__ = [
     "brute_force_row",
     "pack_codes",
     "unpack_codes",
+    "dequant_gemv",
 ]
 
 
@@ -506,3 +507,25 @@ def unpack_codes(words, bits: int, c: int) -> np.ndarray:
                     out[i, 32 * grp + k] = (v >> (3 * k)) & 0x7
         return out
     raise ValueError("packing supports 3 and 4 bits")
+
+
+# ---------------------------------------------------------------------------
+# Using the packed layer -- "GPTQ, with the code open", section "What
+# quantization is, and why anyone bothers": at generation time each weight is
+# turned back into scale * (tick - zero) while the matrix-vector product runs
+# (a batch-1 product is limited by reading the weights, so reading fewer bits
+# is the point).  One ruler per row or per group of input columns; g_idx maps
+# each original input column to its group.
+# ---------------------------------------------------------------------------
+def dequant_gemv(words, bits: int, c: int, scales, zeros, g_idx, x) -> np.ndarray:
+    """y = W_hat x in float64 for a packed layer.
+
+    words: packed codes [r, c * bits / 32] (this project's layout, see
+    pack_codes); scales/zeros [r, n_groups]; g_idx int [c] (group of each
+    input column; all 0 for one ruler per row); x [c].
+    """
+    codes = unpack_codes(words, bits, c)
+    g = np.asarray(g_idx, np.int64)
+    w_hat = dequantize(codes, np.asarray(scales)[:, g], np.asarray(zeros, F64)[:, g])
+    return w_hat @ np.asarray(x, F64)
+

@@ -440,3 +440,30 @@ def test_symmetric_tiny_layers_against_brute_force():
         assert zero == 4
         _, best = ref.brute_force_row(w0, X, scale, zero, 3)
         assert best <= ref.layer_loss_from_x(w0[None], out["w_hat"], X) * (1 + 1e-12)
+
+
+# --- dequantize-on-the-fly product over the packed layer ---
+def test_dequant_gemv_closed_form():
+    # one row, 8 columns, 4 bits, two groups of 4: codes 0..7, rulers (0.5, 2) and (0.25, 5)
+    words = ref.pack_codes(np.arange(8)[None], 4)
+    scales = np.array([[0.5, 0.25]], np.float32)
+    zeros = np.array([[2, 5]])
+    x = np.array([1.0, -1.0, 2.0, 0.5, 4.0, 1.0, -2.0, 3.0])
+    # w_hat = 0.5*(0..3 - 2) = [-1, -0.5, 0, 0.5]; 0.25*(4..7 - 5) = [-0.25, 0, 0.25, 0.5]
+    expect = (-1 * 1 + -0.5 * -1 + 0 * 2 + 0.5 * 0.5) + (-0.25 * 4 + 0 * 1 + 0.25 * -2 + 0.5 * 3)
+    y = ref.dequant_gemv(words, 4, 8, scales, zeros, [0, 0, 0, 0, 1, 1, 1, 1], x)
+    assert y[0] == expect == -0.25
+
+
+@pytest.mark.parametrize("bits,groupsize,act_order", [(4, 16, False), (3, 32, True), (4, -1, True), (3, -1, False)])
+def test_dequant_gemv_matches_the_quantizers_w_hat(bits, groupsize, act_order):
+    rng = np.random.default_rng(40 + bits)
+    r, c = 7, 64
+    X = _correlated_x(rng, 150, c)
+    W0 = rng.standard_normal((r, c)) * 0.02
+    out = ref.gptq_quantize(W0, ref.hessian(X), bits=bits, groupsize=groupsize, act_order=act_order)
+    words = ref.pack_codes(out["codes"], bits)
+    x = rng.standard_normal(c)
+    y = ref.dequant_gemv(words, bits, c, out["scales"], out["zeros"], out["g_idx"], x)
+    np.testing.assert_allclose(y, out["w_hat"] @ x, rtol=1e-12, atol=1e-15)
+
