@@ -14,6 +14,17 @@ oracle timed on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
     python bench.py --copy-probe      # plain copy of known size (PMC calibration)
+    python bench.py --gemv [--gemv-model llama7b|opt175b] [--steps K] [--warmup W]
+
+--gemv measures the dequantizing matrix-vector product over packed layers
+instead: one step = one generated token (batch 1) through every linear layer
+of the named model, each a separate gptq_dequant_gemv launch over its own
+packed words (distinct memory, so the words come from HBM, not cache).  It
+prints its own JSON line: weights/s and effective GB/s for the token, the
+roofline of the largest layer's launch (HIP events around back-to-back
+launches over distinct layers of that shape), the same token through bf16 /
+fp16 torch matrix-vector products for comparison, and the oracle on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -107,6 +118,202 @@ def cpu_baseline(W_dev, X_dev, w, tokens_sample=16384, rows_sample=128):
     }
 
 
+GEMV_MODELS = {
+    # name: (blocks, [(layer, rows, cols), ...] per block, bits, groupsize, x dtype)
+    "llama7b": (32, [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+                     ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008)],
+                4, 128, "bfloat16"),
+    "opt175b": (96, [("q", 12288, 12288), ("k", 12288, 12288), ("v", 12288, 12288), ("out", 12288, 12288),
+                     ("fc1", 49152, 12288), ("fc2", 12288, 49152)],
+                3, 128, "float16"),
+}
+
+
+def gemv_bytes(r: int, c: int, bits: int, groupsize: int, xbytes: int = 2) -> int:
+    """Algorithmic HBM bytes of one launch: packed words, fp32 scales and int32
+    zeros (one per row and group), x once, y once."""
+    G = (c + groupsize - 1) // groupsize if 0 < groupsize < c else 1
+    return r * c * bits // 8 + r * G * 8 + c * xbytes + r * 4
+
+
+def gemv_cpu_baseline(layers, bits, groupsize, xs, total_weights, codes_sample=8_000_000):
+    """The oracle's dequantizing product on a few rows of each layer shape
+    (about codes_sample codes in all), extrapolated to the token by weight
+    count."""
+    import numpy as np
+
+    from oracle import gptq_ref as ref
+    cols = sum({(L["r"], L["c"]): L["c"] for L in layers}.values())
+    rows_sample = max(8, codes_sample // cols)
+    seen, t_sum, w_sum = set(), 0.0, 0
+    for L in layers:
+        key = (L["r"], L["c"])
+        if key in seen:
+            continue
+        seen.add(key)
+        words = L["packed"][:rows_sample].cpu().numpy()
+        sc = L["scales"][:rows_sample].cpu().numpy()
+        zr = L["zeros"][:rows_sample].cpu().numpy()
+        x = xs[L["c"]].float().cpu().numpy()
+        g = np.arange(L["c"]) // groupsize
+        t0 = time.perf_counter()
+        ref.dequant_gemv(words, bits, L["c"], sc, zr, g, x)
+        t_sum += time.perf_counter() - t0
+        w_sum += rows_sample * L["c"]
+    rate = w_sum / t_sum
+    return {
+        "value": rate,
+        "unit": "weights/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{rows_sample} rows of each distinct layer shape ({w_sum} weights, {t_sum:.2f} s); "
+                   f"single-threaded Python unpacking; extrapolated: "
+                   f"{total_weights / rate:.1f} s per token"),
+    }
+
+
+def bench_gemv(args) -> int:
+    import torch
+
+    from post_weight_quantization_23_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_23_amd import build as b
+        b.build()
+    import post_weight_quantization_23_amd as q
+    from synth import inputs as S
+
+    blocks, shapes, bits, gs, xdt = GEMV_MODELS[args.gemv_model]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xdtype = getattr(torch, xdt)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(S.torch_seed(900, 0, 3))
+    layers = []
+    log(f"building {blocks} x {len(shapes)} packed layers of {args.gemv_model} ({bits}-bit, g{gs}) ...")
+    for b in range(blocks):
+        for name, r, c in shapes:
+            G = S.n_groups(c, gs)
+            words = torch.randint(-2 ** 31, 2 ** 31, (r, c * bits // 32), generator=gen, device=dev,
+                                  dtype=torch.int32).view(torch.uint32)
+            scales = (0.02 * 5.0 / (2 ** bits - 1)) * torch.exp(
+                0.3 * torch.randn((r, G), generator=gen, device=dev))
+            zeros = torch.randint(0, 2 ** bits, (r, G), generator=gen, device=dev, dtype=torch.int32)
+            layers.append({"name": f"{name}{b}", "r": r, "c": c, "packed": words, "scales": scales.float(),
+                           "zeros": zeros, "y": torch.empty(r, dtype=torch.float32, device=dev)})
+    xs = {}
+    for _, r, c in shapes:
+        if c not in xs:
+            xs[c] = torch.from_numpy(S.token_host(c, 900 + c % 101, xdt, "t4", outliers=max(1, c // 200),
+                                                  gain=30.0)).to(dev).to(xdtype)
+    torch.cuda.synchronize()
+    total_w = sum(L["r"] * L["c"] for L in layers)
+    total_b = sum(gemv_bytes(L["r"], L["c"], bits, gs) for L in layers)
+    log(f"{len(layers)} layers, {total_w / 1e9:.2f} G weights, {total_b / 1e9:.2f} GB per token")
+
+    def token():
+        for L in layers:
+            q.dequant_gemv(L["packed"], L["scales"], L["zeros"], xs[L["c"]], bits, gs, out=L["y"])
+
+    for _ in range(args.warmup):
+        token()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        token()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_tok = e0.elapsed_time(e1) / args.steps
+    log(f"token: {ms_tok:.4f} ms (events), wall {wall * 1e3 / args.steps:.4f} ms")
+
+    # Dominant kernel: the launch shape with the most bytes per token; its
+    # launches over distinct layers, back to back, bracketed by events.
+    by_shape = {}
+    for L in layers:
+        by_shape.setdefault((L["r"], L["c"]), []).append(L)
+    dom = max(by_shape, key=lambda k: gemv_bytes(k[0], k[1], bits, gs) * len(by_shape[k]))
+    dl = by_shape[dom]
+    reps = max(1, 64 // len(dl))
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(reps):
+        for L in dl:
+            q.dequant_gemv(L["packed"], L["scales"], L["zeros"], xs[L["c"]], bits, gs, out=L["y"])
+    f1.record()
+    torch.cuda.synchronize()
+    us_launch = f0.elapsed_time(f1) * 1e3 / (reps * len(dl))
+    b_launch = gemv_bytes(dom[0], dom[1], bits, gs)
+    achieved = b_launch / (us_launch * 1e-6) / 1e9
+
+    # The same token through 16-bit torch matrix-vector products (weights in
+    # the activation dtype), for the pages' "faster than fp16" comparison.
+    ref16 = None
+    if args.gemv_model == "llama7b":
+        w16 = [torch.empty((L["r"], L["c"]), dtype=xdtype, device=dev).normal_(0.0, 0.02, generator=gen)
+               for L in layers]
+        y16 = {r: torch.empty(r, dtype=xdtype, device=dev) for _, r, _ in shapes}
+
+        def token16():
+            for Wt, L in zip(w16, layers):
+                torch.mv(Wt, xs[L["c"]], out=y16[L["r"]])
+
+        for _ in range(2):
+            token16()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            token16()
+        g1.record()
+        torch.cuda.synchronize()
+        ms16 = g0.elapsed_time(g1) / args.steps
+        ref16 = {"ms_per_token": ms16, "speedup": ms16 / ms_tok,
+                 "what": f"torch.mv on {xdt} weights of the same shapes ({len(layers)} launches, distinct memory)"}
+        del w16
+
+    rec = {
+        "metric": f"dequantizing GEMV, one generated token (batch 1) through {args.gemv_model}'s "
+                  f"{len(layers)} linear layers, {bits}-bit g{gs}: weights/s",
+        "value": total_w / (ms_tok * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_tok,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 dot (codes x activations), f32 sums",
+        "data": "synthetic (seeded random packed words, log-normal scales, uniform zero points, "
+                "Student-t(4) activations with outlier channels)",
+        "config": {"workload": f"{args.gemv_model}_decode_token_{bits}bit_g{gs}", "layers": len(layers),
+                   "weights": total_w, "bytes_per_token": total_b, "x_dtype": xdt},
+        "effective_GBps": total_b / (ms_tok * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": f"dq_gemv_kernel<{bits},*> on the {dom[0]}x{dom[1]} layers ({len(dl)} per token, "
+                      f"{reps * len(dl)} launches back to back between HIP events)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": b_launch,
+            "us_per_launch": us_launch,
+        },
+        "fp16_reference": ref16,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample ...")
+        rec["cpu_baseline"] = gemv_cpu_baseline(layers, bits, gs, xs, total_w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +322,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="llama7b_attn_4096x4096")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--gemv", action="store_true")
+    ap.add_argument("--gemv-model", default="llama7b", choices=sorted(GEMV_MODELS))
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -127,6 +336,8 @@ def main(argv=None) -> int:
     if args.copy_probe:
         copy_probe()
         return 0
+    if args.gemv:
+        return bench_gemv(args)
 
     from post_weight_quantization_23_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):

@@ -14,7 +14,8 @@
  *     inside the block and deferred to one matrix product beyond it;
  *   - section "What quantization is, and why anyone bothers": the asymmetric
  *     min-max ruler, scale = (max - min)/(2^b - 1), the zero point rounded to
- *     a whole tick, w_hat = scale * (q - zero).
+ *     a whole tick, w_hat = scale * (q - zero); and the use of the stored
+ *     ticks at generation, dequantized inside a matrix-vector product.
  *
  * Conventions shared by every call:
  *   - Every pointer argument that names an array is a DEVICE pointer (memory
@@ -172,12 +173,55 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t
  *              little-endian 96-bit value (word 0 = bits 0..31), so codes 10
  *              and 21 straddle two words.
  * Packed along the input (column) axis, one output row at a time.
- * codes  : r x c uint8 (values must fit in `bits`; higher bits are ignored).
- * packed : r x ld_words uint32 out; ld_words >= c * bits / 32.
+ * codes    : r x c uint8 (values must fit in `bits`; higher bits are ignored).
+ * col_perm : int32[c] (nullable).  When given, packed column j holds the code
+ *            of original column col_perm[j] (entries outside 0 .. c-1 are
+ *            clamped).  Passing the act-order permutation of gptq_prepare
+ *            stores the codes in the order the columns were quantized, where
+ *            every group of columns is contiguous -- the layout
+ *            gptq_dequant_gemv reads for act-order layers.
+ * packed   : r x ld_words uint32 out; ld_words >= c * bits / 32.
  * Requires c % 8 == 0 (4-bit) or c % 32 == 0 (3-bit).
  * ------------------------------------------------------------------------ */
-gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
-                      int64_t ld_words, void* stream);
+gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits,
+                      const int32_t* col_perm, uint32_t* packed, int64_t ld_words,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Dequantize-on-the-fly matrix-vector product (batch 1) over packed codes.
+ * Pages: "GPTQ, with the code open", section "What quantization is, and why
+ * anyone bothers" (generation reads every weight once per token; the stored
+ * tick index is turned back into scale * (tick - zero) while multiplying) and
+ * "Post-training quantization", section "Weight-only and weight-and-
+ * activation" (4- or 3-bit weights with 16-bit activations).
+ *
+ *   y[i] = sum_j scales[i, g(j)] * (q[i, j] - zeros[i, g(j)]) * x[src(j)]
+ *
+ * over the packed columns j = 0 .. c-1, where q[i, j] is packed column j of
+ * row i (layout of gptq_pack), g(j) = j / groupsize (0 for one ruler per row)
+ * and src(j) = col_perm[j] when col_perm is given, else j.  For an act-order
+ * layer pack with col_perm = the act-order permutation and pass the same
+ * col_perm here; scales / zeros are then used as gptq_quantize_layer wrote
+ * them (group g covers quantization positions g*groupsize ..).
+ *
+ * packed    : r x ld_words uint32 (gptq_pack output); 4 bits: 16-byte aligned
+ *             base and ld_words % 4 == 0.
+ * bits      : 3 or 4.
+ * scales    : r x ld_groups fp32; zeros: r x ld_groups int32.
+ * groupsize : <= 0 or >= c: one ruler per row; else a multiple of 32, and
+ *             ld_groups >= ceil(c / groupsize).
+ * col_perm  : int32[c] or NULL (entries outside 0 .. c-1 are clamped).
+ * x         : c activations, GPTQ_BF16 or GPTQ_F16 (GPTQ_F32 -> GPTQ_EDTYPE);
+ *             16-byte aligned unless col_perm is given.
+ * y         : fp32[r] out.
+ * Requires c % 32 == 0 and c <= 49152 (GPTQ_EUNSUPPORTED beyond).  c == 0
+ * writes y = 0.  Products are exact and sums are fp32: the result is within
+ * about 64 * 2^-24 * sum_j scale * (q + zero) * |x_j| of the exact value.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int bits,
+                              int64_t ld_words, const float* scales, const int32_t* zeros,
+                              int64_t ld_groups, int64_t groupsize, const int32_t* col_perm,
+                              const void* x, gptq_dtype xt, float* y, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* gptq_status_string(gptq_status s);

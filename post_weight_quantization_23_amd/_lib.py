@@ -28,7 +28,8 @@ SIGNATURES = {
     "gptq_quantize_layer_workspace_size": (C.c_int, [_I64, _I64, _I64, _SZP]),
     "gptq_quantize_layer": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _P, _P, _P, C.c_int, C.c_int, _I64, _I64,
                                       _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "gptq_pack": (C.c_int, [_P, _I64, _I64, C.c_int, _P, _I64, _P]),
+    "gptq_pack": (C.c_int, [_P, _I64, _I64, C.c_int, _P, _P, _I64, _P]),
+    "gptq_dequant_gemv": (C.c_int, [_P, _I64, _I64, C.c_int, _I64, _P, _P, _I64, _I64, _P, _P, C.c_int, _P, _P]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_last_error": (C.c_char_p, []),
 }

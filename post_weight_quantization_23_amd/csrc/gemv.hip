@@ -1,0 +1,403 @@
+// Dequantize-on-the-fly matrix-vector product over packed codes, batch 1:
+//     y[i] = sum_j scale[i, g(j)] * (q[i, j] - zero[i, g(j)]) * x[j]
+// The pages: "GPTQ, with the code open", section "What quantization is, and
+// why anyone bothers" -- a generated token reads every weight once, so the
+// stored tick indices are turned back into scale * (tick - zero) inside the
+// product and the smaller words become a faster read.  The page "Post-training
+// quantization", section "Weight-only and weight-and-activation", names the
+// regime: four-bit (or three-bit) weights, sixteen-bit activations.
+//
+// Design (HBM-bound streaming, one pass over the packed words):
+//   * A "chunk" is 32 consecutive packed columns: 16 bytes at 4 bits, 12 bytes
+//     at 3 bits.  Lane l of a wave owns chunks l, l + 64 S, l + 128 S, ... of
+//     its column slice for every row it visits, so one wave-wide load reads
+//     64 consecutive chunks of a row (1 KiB at 4 bits) and the lane's slice of
+//     x stays in registers across all rows.
+//   * Codes become fp16 subnormals without arithmetic: a field of the packed
+//     word masked into bits p .. p+b-1 of a 16-bit half (exponent bits zero)
+//     is exactly q * 2^(p-24).  Two such halves meet a pair of x values
+//     pre-scaled by 2^(24-p) in one v_dot2_f32_f16, whose products are exact
+//     and whose sum is fp32.  Each 8-code block takes two 32-bit windows of
+//     the packed stream and two masks per window; the pairing (8m+t, 8m+t+4)
+//     is the same for both widths, only the field positions differ.
+//   * x (bf16 or fp16) is rescaled per chunk by a power of two chosen from the
+//     chunk's largest |x| so that every pre-scaled value fits fp16; bf16 and
+//     fp16 significands fit fp16's, so the conversion is exact for every value
+//     within 2^-25 of the chunk maximum (smaller ones fall on fp16's subnormal
+//     grid, an error below 2^-40 of the chunk maximum per value).
+//   * The zero point is taken out once per chunk: sum q x - zero * sum x, with
+//     sum x of the chunk computed once in fp32.
+//   * Rows are visited four at a time; the four partial sums of a wave are
+//     folded with a transposed butterfly (each exchange halves the values per
+//     lane) and, when a row's columns are split over S waves of the
+//     workgroup, summed across waves through LDS in wave order.  The packed
+//     words of the next four rows are loaded before the current ones are used.
+//   * act-order layers are handled by packing their codes in the order the
+//     columns were quantized (groups are then contiguous) and gathering x
+//     through that permutation once per lane.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gptq {
+
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxNch = 3;     // chunks per lane (register budget)
+constexpr int kRows = 4;       // rows per wave visit
+
+struct GemvArgs {
+  const uint32_t* packed;
+  int64_t ldw;            // words per row
+  const float* scales;
+  const int32_t* zeros;
+  int64_t ldg;            // groups per row (row stride of scales / zeros)
+  const int32_t* perm;    // nullable: packed column j holds original column perm[j]
+  const uint16_t* x;      // bf16 or fp16 bits
+  float* y;
+  int r, c, nch;          // rows, columns, 32-column chunks
+  int cpg;                // chunks per group (>= nch: one group per row)
+  int S;                  // waves sharing one row (column split)
+  int G;                  // wave groups per workgroup
+  int nquads;             // ceil(r / 4)
+  int f16x;               // x is fp16 (else bf16)
+};
+
+// Field positions (p of the low half, p of the high half) of the two masks.
+template <int BITS>
+struct Fields;
+template <>
+struct Fields<4> {
+  static constexpr uint32_t M1 = 0x000F000Fu, M2 = 0x00F000F0u;
+  static constexpr int P1LO = 0, P1HI = 0, P2LO = 4, P2HI = 4;
+};
+template <>
+struct Fields<3> {
+  static constexpr uint32_t M1 = 0x00070070u, M2 = 0x00380380u;
+  static constexpr int P1LO = 4, P1HI = 0, P2LO = 7, P2HI = 3;
+};
+
+template <int BITS>
+struct Words;
+template <>
+struct Words<4> {
+  uint32_t w[4];
+};
+template <>
+struct Words<3> {
+  uint32_t w[3];
+};
+
+// Bits s .. s+31 of the 64-bit value hi:lo (v_alignbit_b32).
+GPTQ_DEV uint32_t window(uint32_t hi, uint32_t lo, uint32_t s) { return __builtin_amdgcn_alignbit(hi, lo, s); }
+
+// The two 32-bit windows (A, B) of 8-code block m of a chunk.
+//   4 bits: A = word m, B = word m >> 8.
+//   3 bits: block m spans stream bits 24m .. 24m+23; A starts at bit 24m - 4,
+//           B at bit 24m + 2 of the 96-bit little-endian stream.
+template <int BITS>
+GPTQ_DEV void windows(const Words<BITS>& v, int m, uint32_t& A, uint32_t& B);
+template <>
+GPTQ_DEV void windows<4>(const Words<4>& v, int m, uint32_t& A, uint32_t& B) {
+  A = v.w[m];
+  B = v.w[m] >> 8;
+}
+template <>
+GPTQ_DEV void windows<3>(const Words<3>& v, int m, uint32_t& A, uint32_t& B) {
+  if (m == 0) {
+    A = v.w[0] << 4;
+    B = v.w[0] >> 2;
+  } else if (m == 1) {
+    A = window(v.w[1], v.w[0], 20);
+    B = window(v.w[1], v.w[0], 26);
+  } else if (m == 2) {
+    A = window(v.w[2], v.w[1], 12);
+    B = window(v.w[2], v.w[1], 18);
+  } else {
+    A = v.w[2] >> 4;
+    B = v.w[2] >> 10;
+  }
+}
+
+GPTQ_DEV float dot2(uint32_t codes, half2_t x, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, codes), x, acc, false);
+}
+
+GPTQ_DEV float x_to_f32(uint16_t b, bool f16) {
+  return f16 ? (float)__builtin_bit_cast(_Float16, b) : __uint_as_float((uint32_t)b << 16);
+}
+
+template <int BITS>
+GPTQ_DEV Words<BITS> load_words(const uint32_t* __restrict__ p) {
+  Words<BITS> v;
+  if constexpr (BITS == 4) {
+    const u32x4 t = *reinterpret_cast<const u32x4*>(p);
+    v.w[0] = t[0]; v.w[1] = t[1]; v.w[2] = t[2]; v.w[3] = t[3];
+  } else {
+    v.w[0] = p[0]; v.w[1] = p[1]; v.w[2] = p[2];
+  }
+  return v;
+}
+
+template <int BITS>
+struct RowBuf {
+  Words<BITS> w[kRows][kMaxNch];
+  float s[kRows][kMaxNch];
+  int z[kRows][kMaxNch];
+};
+
+// Words and rulers of rows 4 quad .. 4 quad + 3 for this lane's chunks.  Rows
+// past the end and the quads of idle wave groups read row r-1 (results are
+// dropped); a lane's chunks past the end read the last chunk, and their
+// contribution is zero because their x values are zero and their scale is
+// replaced by 0.  No branches, so every load is issued back to back.
+template <int BITS, int NCH>
+GPTQ_DEV void load_quad(const GemvArgs& a, int quad, const int (&jc)[kMaxNch], const int (&grp)[kMaxNch],
+                        const bool (&jv)[kMaxNch], RowBuf<BITS>& b) {
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int row = __builtin_amdgcn_readfirstlane(min(quad * kRows + i, a.r - 1));
+    const uint32_t* prow = a.packed + (int64_t)row * a.ldw;
+    const float* srow = a.scales + (int64_t)row * a.ldg;
+    const int32_t* zrow = a.zeros + (int64_t)row * a.ldg;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      // 32-bit unsigned offsets from a wave-uniform row base (global_load with saddr)
+      const uint32_t wo = (uint32_t)jc[k] * (4u * BITS), go = (uint32_t)grp[k] * 4u;
+      b.w[i][k] = load_words<BITS>(reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(prow) + wo));
+      const float sc = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(srow) + go);
+      b.s[i][k] = jv[k] ? sc : 0.f;
+      b.z[i][k] = *reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(zrow) + go);
+    }
+  }
+}
+
+// sum_j q_j x_j over one chunk, in units of 2^(8 + ex) (see the x prologue).
+template <int BITS>
+GPTQ_DEV float chunk_dot(const Words<BITS>& v, const half2_t (&xp)[16]) {
+  using F = Fields<BITS>;
+  float d = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    uint32_t A, B;
+    windows<BITS>(v, m, A, B);
+    d = dot2(A & F::M1, xp[4 * m + 0], d);
+    d = dot2(A & F::M2, xp[4 * m + 1], d);
+    d = dot2(B & F::M1, xp[4 * m + 2], d);
+    d = dot2(B & F::M2, xp[4 * m + 3], d);
+  }
+  return d;
+}
+
+// Four row sums spread over the wave -> lane i (i < 4) holds row i's total.
+GPTQ_DEV float fold4(float v0, float v1, float v2, float v3, int lane) {
+  const bool b0 = lane & 1;
+  float ka = b0 ? v1 : v0, kb = b0 ? v3 : v2;
+  const float sa = b0 ? v0 : v1, sb = b0 ? v2 : v3;
+  ka += __shfl_xor(sa, 1);
+  kb += __shfl_xor(sb, 1);
+  const bool b1 = lane & 2;
+  float k = b1 ? kb : ka;
+  const float s = b1 ? ka : kb;
+  k += __shfl_xor(s, 2);
+  k += __shfl_xor(k, 4);
+  k += __shfl_xor(k, 8);
+  k += __shfl_xor(k, 16);
+  k += __shfl_xor(k, 32);
+  return k;
+}
+
+template <int BITS, int NCH>
+__global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
+  using F = Fields<BITS>;
+  __shared__ float red[2][8][4];   // [parity][wave][row]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = wave / a.S, sl = wave - g * a.S;
+
+  // ---- chunk ownership of this lane (jc: clamped index, jv: in range)
+  int jch[kMaxNch], jc[kMaxNch], grp[kMaxNch];
+  bool jv[kMaxNch];
+#pragma unroll
+  for (int k = 0; k < kMaxNch; ++k) {
+    jch[k] = sl * 64 + lane + k * 64 * a.S;
+    jv[k] = jch[k] < a.nch;
+    jc[k] = jv[k] ? jch[k] : a.nch - 1;
+    grp[k] = jc[k] / a.cpg;
+  }
+
+  // ---- first rows' words go out before the x prologue
+  int quad = blockIdx.x * a.G + g;
+  const int qstride = gridDim.x * a.G;
+  const int iters = (a.nquads - (int)blockIdx.x * a.G + qstride - 1) / qstride;
+  RowBuf<BITS> bufA, bufB;
+  load_quad<BITS, NCH>(a, quad, jc, grp, jv, bufA);
+
+  // ---- x prologue: pre-scaled fp16 pairs, chunk sums and exponents
+  half2_t xp[NCH][16];
+  float sx[NCH];
+  int ex[NCH];
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    float xf[32];
+    if (jv[k]) {
+      const int64_t c0 = (int64_t)jch[k] * 32;
+      if (a.perm) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const int src = min(max(a.perm[c0 + i], 0), a.c - 1);
+          xf[i] = x_to_f32(a.x[src], a.f16x);
+        }
+      } else {
+        const u32x4* px = reinterpret_cast<const u32x4*>(a.x + c0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 t = px[q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xf[8 * q + 2 * e] = x_to_f32((uint16_t)(t[e] & 0xFFFFu), a.f16x);
+            xf[8 * q + 2 * e + 1] = x_to_f32((uint16_t)(t[e] >> 16), a.f16x);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) xf[i] = 0.f;
+    }
+    float mx = 0.f, sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      mx = fmaxf(mx, fabsf(xf[i]));
+      sum += xf[i];
+    }
+    // |x| < 2^e1 for every x of the chunk (e1 = frexp exponent of the max).
+    const int e1 = __builtin_amdgcn_frexp_expf(mx);
+    ex[k] = e1;
+    sx[k] = __builtin_ldexpf(sum, -8 - e1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int plo = (t & 1) ? F::P2LO : F::P1LO;
+        const int phi = (t & 1) ? F::P2HI : F::P1HI;
+        const float lo = __builtin_ldexpf(xf[8 * m + t], 16 - plo - e1);
+        const float hi = __builtin_ldexpf(xf[8 * m + t + 4], 16 - phi - e1);
+        xp[k][4 * m + t] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+      }
+    }
+  }
+
+  auto compute = [&](const RowBuf<BITS>& b, int qd, int parity) {
+    float acc[kRows];
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < NCH; ++k) {
+        const float d = chunk_dot<BITS>(b.w[i][k], xp[k]);
+        const float t = __builtin_fmaf(-(float)b.z[i][k], sx[k], d);
+        // scale first, then undo the chunk's power of two: no intermediate
+        // overflow for activations near the top of bf16's range
+        s += __builtin_ldexpf(t * b.s[i][k], 8 + ex[k]);
+      }
+      acc[i] = s;
+    }
+    float tot = fold4(acc[0], acc[1], acc[2], acc[3], lane);
+    if (a.S > 1) {
+      if (lane < kRows) red[parity][wave][lane] = tot;
+      __syncthreads();
+      if (sl == 0) {
+        tot = red[parity][wave][lane & 3];
+        for (int w = 1; w < a.S; ++w) tot += red[parity][wave + w][lane & 3];
+      }
+    }
+    const int row = qd * kRows + lane;
+    if (sl == 0 && lane < kRows && qd < a.nquads && row < a.r) a.y[row] = tot;
+  };
+
+  for (int it = 0; it < iters; it += 2) {
+    if (it + 1 < iters) load_quad<BITS, NCH>(a, quad + qstride, jc, grp, jv, bufB);
+    compute(bufA, quad, 0);
+    if (it + 2 < iters) load_quad<BITS, NCH>(a, quad + 2 * qstride, jc, grp, jv, bufA);
+    if (it + 1 < iters) compute(bufB, quad + qstride, 1);
+    quad += 2 * qstride;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_f32_kernel(float* y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) y[i] = 0.f;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace
+
+GemvPlan plan_gemv(int64_t c) {
+  GemvPlan p{};
+  const int64_t nch = c / 32;
+  p.S = 0;
+  for (int S = 1; S <= 8; S *= 2) {
+    if ((nch + 64 * S - 1) / (64 * S) <= kMaxNch) {
+      p.S = S;
+      break;
+    }
+  }
+  if (p.S) p.nch_lane = (int)((nch + 64 * p.S - 1) / (64 * p.S));
+  return p;
+}
+
+void launch_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int bits, int64_t ld_words,
+                         const float* scales, const int32_t* zeros, int64_t ld_groups, int64_t groupsize,
+                         const int32_t* perm, const void* x, int x_f16, float* y, hipStream_t s) {
+  if (c == 0) {
+    hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((r + 255) / 256)), dim3(256), 0, s, y, r);
+    return;
+  }
+  const GemvPlan p = plan_gemv(c);
+  GemvArgs a;
+  a.packed = packed;
+  a.ldw = ld_words;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.ldg = ld_groups;
+  a.perm = perm;
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = y;
+  a.r = (int)r;
+  a.c = (int)c;
+  a.nch = (int)(c / 32);
+  a.cpg = (groupsize > 0 && groupsize < c) ? (int)(groupsize / 32) : a.nch;
+  a.S = p.S;
+  const int waves = p.S > 4 ? p.S : 4;
+  a.G = waves / p.S;
+  a.nquads = (int)((r + kRows - 1) / kRows);
+  a.f16x = x_f16;
+  const int64_t want = (a.nquads + a.G - 1) / a.G;
+  const int64_t cap = (int64_t)device_cus() * (waves > 4 ? 1 : 2);
+  const unsigned grid = (unsigned)(want < cap ? want : cap);
+  const dim3 block(64 * waves);
+  if (bits == 4) {
+    if (p.nch_lane == 1) hipLaunchKernelGGL((dq_gemv_kernel<4, 1>), dim3(grid), block, 0, s, a);
+    else if (p.nch_lane == 2) hipLaunchKernelGGL((dq_gemv_kernel<4, 2>), dim3(grid), block, 0, s, a);
+    else hipLaunchKernelGGL((dq_gemv_kernel<4, 3>), dim3(grid), block, 0, s, a);
+  } else {
+    if (p.nch_lane == 1) hipLaunchKernelGGL((dq_gemv_kernel<3, 1>), dim3(grid), block, 0, s, a);
+    else if (p.nch_lane == 2) hipLaunchKernelGGL((dq_gemv_kernel<3, 2>), dim3(grid), block, 0, s, a);
+    else hipLaunchKernelGGL((dq_gemv_kernel<3, 3>), dim3(grid), block, 0, s, a);
+  }
+}
+
+}  // namespace gptq

@@ -182,8 +182,8 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t
 }
 
 // ------------------------------------------------------------------ pack
-gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
-                      int64_t ld_words, void* stream) {
+gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, const int32_t* col_perm,
+                      uint32_t* packed, int64_t ld_words, void* stream) {
   const char* fn = "gptq_pack";
   if (r < 0 || c < 0) return fail(GPTQ_EINVAL, fn, "negative size");
   if (bits != 3 && bits != 4) return fail(GPTQ_EUNSUPPORTED, fn, "packing supports 3 and 4 bits");
@@ -194,7 +194,41 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint
   if (r == 0 || c == 0) return ok();
   if (!codes || !packed) return fail(GPTQ_EINVAL, fn, "codes or packed is NULL");
   if (!aligned(codes, 16) || !aligned(packed, 4)) return fail(GPTQ_EALIGN, fn, "codes must be 16-byte aligned");
-  gptq::launch_pack(codes, r, c, bits, packed, ld_words, reinterpret_cast<hipStream_t>(stream));
+  if (col_perm && !aligned(col_perm, 4)) return fail(GPTQ_EALIGN, fn, "col_perm misaligned");
+  gptq::launch_pack(codes, r, c, bits, col_perm, packed, ld_words, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
+// ------------------------------------------------------------------ dequantizing product
+gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int bits, int64_t ld_words,
+                              const float* scales, const int32_t* zeros, int64_t ld_groups, int64_t groupsize,
+                              const int32_t* col_perm, const void* x, gptq_dtype xt, float* y, void* stream) {
+  const char* fn = "gptq_dequant_gemv";
+  if (r < 0 || c < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (bits != 3 && bits != 4) return fail(GPTQ_EUNSUPPORTED, fn, "bits must be 3 or 4");
+  if (!valid_dtype(xt)) return fail(GPTQ_EINVAL, fn, "xt must be a gptq_dtype");
+  if (xt == GPTQ_F32) return fail(GPTQ_EDTYPE, fn, "x must be GPTQ_BF16 or GPTQ_F16 (16-bit activations)");
+  if (c % 32 != 0) return fail(GPTQ_ESHAPE, fn, "c % 32 != 0");
+  if (r > kMaxRows) return fail(GPTQ_EUNSUPPORTED, fn, "r too large");
+  if (c > 0 && gptq::plan_gemv(c).S == 0) return fail(GPTQ_EUNSUPPORTED, fn, "c > 49152");
+  const bool grouped = groupsize > 0 && groupsize < c;
+  if (grouped && groupsize % 32 != 0) return fail(GPTQ_EUNSUPPORTED, fn, "groupsize must be a multiple of 32");
+  const int64_t n_groups = grouped ? (c + groupsize - 1) / groupsize : 1;
+  if (r == 0) return ok();
+  if (!y) return fail(GPTQ_EINVAL, fn, "y is NULL");
+  if (!aligned(y, 4)) return fail(GPTQ_EALIGN, fn, "y misaligned");
+  if (c > 0) {
+    if (ld_words < c * bits / 32) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
+    if (ld_groups < n_groups) return fail(GPTQ_ESHAPE, fn, "ld_groups < number of groups");
+    if (!packed || !scales || !zeros || !x) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
+    if (bits == 4 && (!aligned(packed, 16) || ld_words % 4 != 0))
+      return fail(GPTQ_EALIGN, fn, "4-bit words need a 16-byte aligned base and ld_words % 4 == 0");
+    if (!aligned(packed, 4) || !aligned(scales, 4) || !aligned(zeros, 4) || (col_perm && !aligned(col_perm, 4)))
+      return fail(GPTQ_EALIGN, fn, "misaligned pointer");
+    if (!aligned(x, col_perm ? 2 : 16)) return fail(GPTQ_EALIGN, fn, "x must be 16-byte aligned");
+  }
+  gptq::launch_dequant_gemv(packed, r, c, bits, ld_words, scales, zeros, ld_groups, groupsize, col_perm, x,
+                            xt == GPTQ_F16 ? 1 : 0, y, reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);
 }
 

@@ -68,7 +68,18 @@ struct QuantArgs {
 void launch_quantize(const QuantArgs& a, hipStream_t s);
 
 // --- Pack (pack.hip) ---
-void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
-                 int64_t ld_words, hipStream_t s);
+// perm (nullable): packed column j takes the code of original column perm[j].
+void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, const int32_t* perm,
+                 uint32_t* packed, int64_t ld_words, hipStream_t s);
+
+// --- Dequantize-on-the-fly product (gemv.hip) ---
+struct GemvPlan {
+  int S;         // waves sharing one row's columns (0: c too large)
+  int nch_lane;  // 32-column chunks per lane
+};
+GemvPlan plan_gemv(int64_t c);
+void launch_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int bits, int64_t ld_words,
+                         const float* scales, const int32_t* zeros, int64_t ld_groups, int64_t groupsize,
+                         const int32_t* perm, const void* x, int x_f16, float* y, hipStream_t s);
 
 }  // namespace gptq

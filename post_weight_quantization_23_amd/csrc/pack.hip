@@ -5,7 +5,10 @@
 //   3 bits: 32 codes per 3 words, code k in bits 3k .. 3k+2 of the
 //           little-endian 96-bit value.
 // Streaming kernel: each thread turns one 8-byte (4-bit) or 32-byte (3-bit)
-// run of codes into one or three words.
+// run of codes into one or three words.  With a column permutation (act-order
+// layers packed in the order their columns were quantized, so that groups are
+// contiguous for the dequantizing product) each thread gathers its codes byte
+// by byte instead.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -60,10 +63,42 @@ __global__ __launch_bounds__(256) void pack3_kernel(const uint8_t* __restrict__ 
   o[2] = (uint32_t)hi;
 }
 
+// Packed column j takes the code of original column perm[j]; one thread per
+// 32 packed columns (one 4-bit quad of words or one 3-bit triple).
+__global__ __launch_bounds__(256) void pack_perm_kernel(const uint8_t* __restrict__ codes, int64_t r,
+                                                        int64_t c, int bits,
+                                                        const int32_t* __restrict__ perm,
+                                                        uint32_t* __restrict__ out, int64_t ldw) {
+  const int64_t nch = (c + 31) / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= r * nch) return;
+  const int64_t row = idx / nch, ch = idx % nch;
+  const uint8_t* src = codes + row * c;
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  const int n = (int)min((int64_t)32, c - ch * 32);
+  for (int k = 0; k < n; ++k) {
+    const int64_t col = min(max((int64_t)perm[ch * 32 + k], (int64_t)0), c - 1);  // entries outside 0..c-1 clamp
+    const uint32_t v = (uint32_t)src[col] & mask;
+    const int bit = bits * k;
+    w[bit >> 5] |= v << (bit & 31);
+    if ((bit & 31) + bits > 32) w[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+  }
+  uint32_t* o = out + row * ldw + ch * bits;
+  const int nw = (n * bits + 31) / 32;
+  for (int t = 0; t < nw; ++t) o[t] = w[t];
+}
+
 }  // namespace
 
-void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, uint32_t* packed,
-                 int64_t ld_words, hipStream_t s) {
+void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, const int32_t* perm,
+                 uint32_t* packed, int64_t ld_words, hipStream_t s) {
+  if (perm) {
+    const int64_t n = r * ((c + 31) / 32);
+    hipLaunchKernelGGL(pack_perm_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, r, c,
+                       bits, perm, packed, ld_words);
+    return;
+  }
   if (bits == 4) {
     const int64_t n = r * (c / 8);
     hipLaunchKernelGGL(pack4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, r, c,

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import GPTQ_BF16, GPTQ_F16, GPTQ_F32, GPTQError
 
-__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "Workspace",
+__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "Workspace",
            "NotPositiveDefinite", "GPTQError"]
 
 _DT = {torch.float32: GPTQ_F32, torch.bfloat16: GPTQ_BF16, torch.float16: GPTQ_F16}
@@ -156,14 +156,57 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor | None, 
             "row_loss": row_loss}
 
 
-def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Pack uint8 codes [r, c] into uint32 words [r, c*bits/32] (layout in include/gptq.h)."""
+def pack(codes: torch.Tensor, bits: int, out: torch.Tensor | None = None,
+         perm: torch.Tensor | None = None) -> torch.Tensor:
+    """Pack uint8 codes [r, c] into uint32 words [r, c*bits/32] (layout in include/gptq.h).
+
+    perm (int32 [c], optional): packed column j takes the code of column
+    perm[j] -- pass the act-order permutation to get the layout dequant_gemv
+    reads for act-order layers."""
     _need(codes, "codes", torch.uint8, 2)
     if not codes.is_contiguous():
         raise ValueError("codes must be contiguous")
     r, c = codes.shape
+    if perm is not None:
+        _need(perm, "perm", torch.int32, 1, codes.device)
+        if perm.numel() != c or not perm.is_contiguous():
+            raise ValueError("perm must be a contiguous int32 vector of length c")
     nw = c * bits // 32
     if out is None:
         out = torch.empty((r, nw), dtype=torch.uint32, device=codes.device)
-    _lib.call("gptq_pack", _ptr(codes), r, c, int(bits), _ptr(out), out.stride(0), _stream())
+    _lib.call("gptq_pack", _ptr(codes), r, c, int(bits), _ptr(perm), _ptr(out), out.stride(0), _stream())
+    return out
+
+
+def dequant_gemv(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, x: torch.Tensor, bits: int,
+                 groupsize: int, perm: torch.Tensor | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = W_hat x for a packed layer, dequantizing inside the product (fp32 [r]).
+
+    packed [r, >= c*bits/32] uint32 (pack output), scales fp32 / zeros int32
+    [r, n_groups], x bf16 or fp16 [c], perm as given to pack (act-order)."""
+    _need(packed, "packed", torch.uint32, 2)
+    dev = packed.device
+    _need(scales, "scales", torch.float32, 2, dev)
+    _need(zeros, "zeros", torch.int32, 2, dev)
+    _need(x, "x", None, 1, dev)
+    if x.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("x must be bfloat16 or float16")
+    if not x.is_contiguous() or packed.stride(1) != 1 or scales.stride(1) != 1 or zeros.stride(1) != 1:
+        raise ValueError("x and the rows of packed / scales / zeros must be contiguous")
+    if scales.shape != zeros.shape or scales.stride() != zeros.stride():
+        raise ValueError("scales and zeros must have the same shape and strides")
+    r, c = packed.shape[0], x.numel()
+    if scales.shape[0] != r:
+        raise ValueError("scales / zeros need one row per packed row")
+    if perm is not None:
+        _need(perm, "perm", torch.int32, 1, dev)
+        if perm.numel() != c or not perm.is_contiguous():
+            raise ValueError("perm must be a contiguous int32 vector of length c")
+    if out is None:
+        out = torch.empty(r, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, 1, dev)
+    if out.numel() != r or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 vector of length r")
+    _lib.call("gptq_dequant_gemv", _ptr(packed), r, c, int(bits), packed.stride(0), _ptr(scales), _ptr(zeros),
+              scales.stride(0), int(groupsize), _ptr(perm), _ptr(x), _DT[x.dtype], _ptr(out), _stream())
     return out

@@ -176,3 +176,53 @@ def workload_device(w: Workload, layer: int = 0, tokens: int | None = None, devi
     X = activations_device(n, w.cols, w.x_kind, w.outliers, w.outlier_gain, w.wid, layer,
                            w.x_dtype, device)
     return W, X
+
+
+# --------------------------------------------------------------------------
+# Packed layers for the dequantizing matrix-vector product (one generated
+# token through a quantized linear layer).  Codes are uniform ticks; scales
+# are log-normal around the tick width of a 128-weight N(0, 0.02^2) row slice
+# (range ~ 5 sigma over 2^b - 1 ticks); zero points are uniform ticks; the
+# act-order permutation is uniform.  x is one token of the activation recipe
+# above.  Seeds: SeedSequence([seed, 0, 3]) for the layer, ([seed, 0, 4]) for x.
+# --------------------------------------------------------------------------
+def n_groups(cols: int, groupsize: int) -> int:
+    return (cols + groupsize - 1) // groupsize if 0 < groupsize < cols else 1
+
+
+def packed_layer_host(rows: int, cols: int, bits: int, groupsize: int, seed: int, act_order: bool = False):
+    """(codes uint8 [rows, cols], scales fp32 [rows, G], zeros int32 [rows, G], perm int32 [cols] | None)."""
+    rng = np.random.default_rng(seed_sequence(seed, 0, 3))
+    G = n_groups(cols, groupsize)
+    codes = rng.integers(0, 2 ** bits, size=(rows, cols), dtype=np.uint8)
+    width = 0.02 * 5.0 / (2 ** bits - 1)
+    scales = (width * np.exp(0.3 * rng.standard_normal((rows, G)))).astype(np.float32)
+    zeros = rng.integers(0, 2 ** bits, size=(rows, G)).astype(np.int32)
+    perm = rng.permutation(cols).astype(np.int32) if act_order else None
+    return codes, scales, zeros, perm
+
+
+def packed_layer_device(rows: int, cols: int, bits: int, groupsize: int, seed: int, act_order: bool = False,
+                        device="cuda"):
+    """Device twin of packed_layer_host for full-size shapes (torch generator)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(torch_seed(seed, 0, 3))
+    G = n_groups(cols, groupsize)
+    codes = torch.randint(0, 2 ** bits, (rows, cols), generator=g, device=device, dtype=torch.uint8)
+    width = 0.02 * 5.0 / (2 ** bits - 1)
+    scales = width * torch.exp(0.3 * torch.randn((rows, G), generator=g, device=device))
+    zeros = torch.randint(0, 2 ** bits, (rows, G), generator=g, device=device, dtype=torch.int32)
+    perm = torch.randperm(cols, generator=g, device=device).to(torch.int32) if act_order else None
+    return codes, scales.float(), zeros, perm
+
+
+def token_host(cols: int, seed: int, dtype: str, kind: str = "t4", outliers: int = 0, gain: float = 1.0):
+    """One activation vector [cols] (float32 values representable in dtype)."""
+    rng = np.random.default_rng(seed_sequence(seed, 0, 4))
+    x = _student_t4(rng, (cols,)) if kind != "normal" else rng.standard_normal(cols)
+    if kind == "t4_relu":
+        x = np.maximum(x - T4_Q60, 0.0)
+    if outliers:
+        x[outlier_channels(cols, outliers, seed, 0)] *= gain
+    return _round_to(x, dtype)

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_symbols_are_exported(lib):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -114,13 +114,41 @@ def test_quantize_argument_errors(lib):
 
 def test_pack_argument_errors(lib):
     f = "gptq_pack"
-    assert _st(lib, f, ALIGNED, 4, 12, 4, ALIGNED, 2, None) == 3     # c % 8
-    assert _st(lib, f, ALIGNED, 4, 48, 3, ALIGNED, 5, None) == 3     # c % 32
-    assert _st(lib, f, ALIGNED, 4, 64, 3, ALIGNED, 5, None) == 3     # ld_words < 6
-    assert _st(lib, f, ALIGNED, 4, 64, 8, ALIGNED, 16, None) == 5    # bits
-    assert _st(lib, f, None, 4, 64, 4, ALIGNED, 8, None) == 1
-    assert _st(lib, f, C.c_void_p(0x10008), 4, 64, 4, ALIGNED, 8, None) == 4
-    assert _st(lib, f, None, 0, 64, 4, None, 8, None) == 0
+    A = ALIGNED
+    assert _st(lib, f, A, 4, 12, 4, None, A, 2, None) == 3     # c % 8
+    assert _st(lib, f, A, 4, 48, 3, None, A, 5, None) == 3     # c % 32
+    assert _st(lib, f, A, 4, 64, 3, None, A, 5, None) == 3     # ld_words < 6
+    assert _st(lib, f, A, 4, 64, 8, None, A, 16, None) == 5    # bits
+    assert _st(lib, f, None, 4, 64, 4, None, A, 8, None) == 1
+    assert _st(lib, f, C.c_void_p(0x10008), 4, 64, 4, None, A, 8, None) == 4
+    assert _st(lib, f, A, 4, 64, 4, C.c_void_p(0x10002), A, 8, None) == 4   # col_perm alignment
+    assert _st(lib, f, None, 0, 64, 4, None, None, 8, None) == 0
+
+
+def test_dequant_gemv_argument_errors(lib):
+    f = "gptq_dequant_gemv"
+    A = ALIGNED
+
+    def g(packed=A, r=8, c=256, bits=4, ldw=32, s=A, z=A, ldg=2, gs=128, perm=None, x=A, xt=1, y=A):
+        return _st(lib, f, packed, r, c, bits, ldw, s, z, ldg, gs, perm, x, xt, y, None)
+
+    assert g(r=0, y=None) == 0                 # nothing to do
+    assert g(r=-1) == 1 and g(c=-32) == 1
+    assert g(bits=2) == 5 and g(bits=8) == 5
+    assert g(xt=0) == 2                        # fp32 activations are not a 16-bit input
+    assert g(xt=7) == 1
+    assert g(c=48, ldw=6) == 3                 # c % 32
+    assert g(c=49152 + 32, ldw=6148, ldg=385) == 5
+    assert g(gs=48) == 5                       # groupsize not a multiple of 32
+    assert g(ldw=31) == 3                      # ld_words < c * bits / 32
+    assert g(ldg=1) == 3                       # 2 groups of 128
+    assert g(gs=-1, ldg=1) != 3 and g(gs=256, ldg=1) != 3 and g(gs=512, ldg=1) != 3
+    assert g(packed=None) == 1 and g(s=None) == 1 and g(z=None) == 1 and g(x=None) == 1 and g(y=None) == 1
+    assert g(packed=C.c_void_p(0x10004)) == 4  # 4-bit words need 16-byte alignment
+    assert g(ldw=34) == 4                      # ... and ld_words % 4 == 0
+    assert g(bits=3, ldw=24, packed=C.c_void_p(0x10004), y=C.c_void_p(0x10002)) == 4
+    assert g(x=C.c_void_p(0x10002)) == 4       # x 16-byte aligned without perm
+    assert g(perm=C.c_void_p(0x10002)) == 4
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -130,3 +158,6 @@ def test_python_binding_rejects_cpu_tensors():
         gptq.hessian_accumulate(torch.zeros(4, 4), torch.zeros(2, 4))
     with pytest.raises(ValueError):
         gptq.pack(torch.zeros(2, 8, dtype=torch.uint8), 4)
+    with pytest.raises(ValueError):
+        gptq.dequant_gemv(torch.zeros(2, 4, dtype=torch.uint32), torch.zeros(2, 1), torch.zeros(2, 1, dtype=torch.int32),
+                          torch.zeros(32, dtype=torch.bfloat16), 4, -1)

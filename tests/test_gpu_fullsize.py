@@ -16,7 +16,10 @@ gptq_pack -- checked on outputs the oracle can compute one by one:
           0.1 %), scales within 1e-5 relative, g_idx identical, W_hat and the
           per-row loss; the layer objective ||(W - W_hat) X||^2 of those rows
           within 1e-3 relative of the oracle's;
-  pack  : the sampled rows' words against the oracle's packing.
+  pack  : the sampled rows' words against the oracle's packing;
+  gemv  : the dequantizing product over the packed layer (act-order layers
+          packed in quantization order) against the oracle's product on the
+          sampled rows, |dy| <= 2^-17 sum scale (q + zero) |x|.
 """
 import numpy as np
 import pytest
@@ -138,3 +141,21 @@ def test_full_size_layer(name, full_u):
     # ---- packing of the sampled rows
     words = packed.view(torch.int32)[seld].cpu().numpy().view(np.uint32)
     np.testing.assert_array_equal(words.astype(np.uint64), ref.pack_codes(codes, w.bits).astype(np.uint64))
+
+    # ---- the dequantizing product over this layer's packed words
+    xg = S.token_host(c, 900 + w.wid, w.x_dtype, "t4", outliers=max(1, c // 200), gain=30.0)
+    xd = torch.from_numpy(xg).cuda().to(getattr(torch, w.x_dtype))
+    if w.act_order:
+        pk = q.pack(out["codes"], w.bits, perm=perm)
+        y = q.dequant_gemv(pk, out["scales"], out["zeros"], xd, w.bits, w.groupsize, perm=perm)
+    else:
+        y = q.dequant_gemv(packed, out["scales"], out["zeros"], xd, w.bits, w.groupsize)
+    y_sel = y[seld].double().cpu().numpy()
+    g = res["g_idx"]
+    y_ref = ref.dequant_gemv(ref.pack_codes(codes, w.bits), w.bits, c, scales, zeros, g, xg)
+    bound = (scales[:, g].astype(np.float64) * (codes.astype(np.float64) + zeros[:, g])) @ np.abs(
+        xg.astype(np.float64))
+    worst = float(np.max(np.abs(y_sel - y_ref) / bound))
+    print(f"  dequantizing product on the sampled rows: max |dy| / bound {worst:.3g}", flush=True)
+    assert worst <= 2.0 ** -17
+
