@@ -214,36 +214,55 @@ def bench_gemv(args) -> int:
         for L in layers:
             q.dequant_gemv(L["packed"], L["scales"], L["zeros"], xs[L["c"]], bits, gs, out=L["y"])
 
-    for _ in range(args.warmup):
+    # Eager launches are bound by Python's per-call cost (~10 us); the token
+    # is captured once in a HIP graph and replayed, as a decode loop would.
+    token()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
         token()
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / 3
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        token()
+    for _ in range(args.warmup):
+        graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for _ in range(args.steps):
-        token()
+        graph.replay()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_tok = e0.elapsed_time(e1) / args.steps
-    log(f"token: {ms_tok:.4f} ms (events), wall {wall * 1e3 / args.steps:.4f} ms")
+    log(f"token: {ms_tok:.4f} ms (graph replay, events), wall {wall * 1e3 / args.steps:.4f} ms, "
+        f"eager launches {ms_eager:.4f} ms")
 
     # Dominant kernel: the launch shape with the most bytes per token; its
-    # launches over distinct layers, back to back, bracketed by events.
+    # launches over distinct layers, back to back in one graph, bracketed by
+    # events.
     by_shape = {}
     for L in layers:
         by_shape.setdefault((L["r"], L["c"]), []).append(L)
     dom = max(by_shape, key=lambda k: gemv_bytes(k[0], k[1], bits, gs) * len(by_shape[k]))
     dl = by_shape[dom]
     reps = max(1, 64 // len(dl))
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        for _ in range(reps):
+            for L in dl:
+                q.dequant_gemv(L["packed"], L["scales"], L["zeros"], xs[L["c"]], bits, gs, out=L["y"])
+    g2.replay()
     f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     f0.record()
-    for _ in range(reps):
-        for L in dl:
-            q.dequant_gemv(L["packed"], L["scales"], L["zeros"], xs[L["c"]], bits, gs, out=L["y"])
+    for _ in range(4):
+        g2.replay()
     f1.record()
     torch.cuda.synchronize()
-    us_launch = f0.elapsed_time(f1) * 1e3 / (reps * len(dl))
+    us_launch = f0.elapsed_time(f1) * 1e3 / (4 * reps * len(dl))
     b_launch = gemv_bytes(dom[0], dom[1], bits, gs)
     achieved = b_launch / (us_launch * 1e-6) / 1e9
 
@@ -291,9 +310,11 @@ def bench_gemv(args) -> int:
         "config": {"workload": f"{args.gemv_model}_decode_token_{bits}bit_g{gs}", "layers": len(layers),
                    "weights": total_w, "bytes_per_token": total_b, "x_dtype": xdt},
         "effective_GBps": total_b / (ms_tok * 1e-3) / 1e9,
+        "ms_per_token_eager_launches": ms_eager,
         "roofline": {
-            "kernel": f"dq_gemv_kernel<{bits},*> on the {dom[0]}x{dom[1]} layers ({len(dl)} per token, "
-                      f"{reps * len(dl)} launches back to back between HIP events)",
+            "kernel": f"dq_gemv_kernel<{bits},*> on the {dom[0]}x{dom[1]} layers ({len(dl)} per token; "
+                      f"{4 * reps * len(dl)} launches back to back in graph replays between HIP events, "
+                      f"gaps between launches included)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": PEAK_HBM_GBS,

@@ -13,25 +13,30 @@
 //     its column slice for every row it visits, so one wave-wide load reads
 //     64 consecutive chunks of a row (1 KiB at 4 bits) and the lane's slice of
 //     x stays in registers across all rows.
-//   * Codes become fp16 subnormals without arithmetic: a field of the packed
-//     word masked into bits p .. p+b-1 of a 16-bit half (exponent bits zero)
-//     is exactly q * 2^(p-24).  Two such halves meet a pair of x values
-//     pre-scaled by 2^(24-p) in one v_dot2_f32_f16, whose products are exact
-//     and whose sum is fp32.  Each 8-code block takes two 32-bit windows of
-//     the packed stream and two masks per window; the pairing (8m+t, 8m+t+4)
-//     is the same for both widths, only the field positions differ.
+//   * Codes become fp16 values with two bit operations and one packed add:
+//     a field of the packed word masked into bits p .. p+b-1 of a 16-bit half
+//     and OR-ed with the exponent of 1024 reads as 1024 + q 2^p, and
+//     subtracting 1024 leaves q 2^p exactly.  Two such halves meet a pair of
+//     x values pre-scaled by 2^(16-p-e) in one v_dot2_f32_f16: the products
+//     q x 2^(16-e) are exact and the sums are fp32.  (The codes are kept out
+//     of fp16's subnormal range on purpose: the dot instruction's products
+//     with subnormal inputs are not exact.)  Each 8-code block takes two
+//     32-bit windows of the packed stream and two masks per window; the
+//     pairing (8m+t, 8m+t+4) is the same for both widths, only the field
+//     positions differ.
 //   * x (bf16 or fp16) is rescaled per chunk by a power of two chosen from the
 //     chunk's largest |x| so that every pre-scaled value fits fp16; bf16 and
 //     fp16 significands fit fp16's, so the conversion is exact for every value
-//     within 2^-25 of the chunk maximum (smaller ones fall on fp16's subnormal
-//     grid, an error below 2^-40 of the chunk maximum per value).
+//     within 2^-29 of the chunk maximum (smaller ones fall on fp16's subnormal
+//     grid, where they contribute below 2^-29 of the chunk maximum each).
 //   * The zero point is taken out once per chunk: sum q x - zero * sum x, with
 //     sum x of the chunk computed once in fp32.
 //   * Rows are visited four at a time; the four partial sums of a wave are
 //     folded with a transposed butterfly (each exchange halves the values per
 //     lane) and, when a row's columns are split over S waves of the
-//     workgroup, summed across waves through LDS in wave order.  The packed
-//     words of the next four rows are loaded before the current ones are used.
+//     workgroup, summed across waves through LDS in wave order.  Two row
+//     quads are in flight per wave: the words of the next quad are loaded
+//     before the current one is used.
 //   * act-order layers are handled by packing their codes in the order the
 //     columns were quantized (groups are then contiguous) and gathering x
 //     through that permutation once per lane.
@@ -124,10 +129,6 @@ GPTQ_DEV float dot2(uint32_t codes, half2_t x, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, codes), x, acc, false);
 }
 
-GPTQ_DEV float x_to_f32(uint16_t b, bool f16) {
-  return f16 ? (float)__builtin_bit_cast(_Float16, b) : __uint_as_float((uint32_t)b << 16);
-}
-
 template <int BITS>
 GPTQ_DEV Words<BITS> load_words(const uint32_t* __restrict__ p) {
   Words<BITS> v;
@@ -173,19 +174,30 @@ GPTQ_DEV void load_quad(const GemvArgs& a, int quad, const int (&jc)[kMaxNch], c
   }
 }
 
-// sum_j q_j x_j over one chunk, in units of 2^(8 + ex) (see the x prologue).
+// Field under mask M of window W as the fp16 pair (q_lo 2^p_lo, q_hi 2^p_hi):
+// exponent of 1024 OR-ed in, 1024 subtracted (exact: the result has at most
+// 11 significant bits).
+// `magic` is 0x64006400 held in a VGPR, so that mask-and-or is one
+// v_and_or_b32 (its other constant, the mask, takes the one scalar operand).
+GPTQ_DEV uint32_t code_pair(uint32_t W, uint32_t M, uint32_t magic) {
+  const half2_t h = __builtin_bit_cast(half2_t, (W & M) | magic);
+  const half2_t k = {(_Float16)1024.0f, (_Float16)1024.0f};
+  return __builtin_bit_cast(uint32_t, h - k);
+}
+
+// sum_j q_j x_j over one chunk, in units of 2^(e - 16) (see the x prologue).
 template <int BITS>
-GPTQ_DEV float chunk_dot(const Words<BITS>& v, const half2_t (&xp)[16]) {
+GPTQ_DEV float chunk_dot(const Words<BITS>& v, const uint32_t (&xp)[16], uint32_t magic) {
   using F = Fields<BITS>;
   float d = 0.f;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     uint32_t A, B;
     windows<BITS>(v, m, A, B);
-    d = dot2(A & F::M1, xp[4 * m + 0], d);
-    d = dot2(A & F::M2, xp[4 * m + 1], d);
-    d = dot2(B & F::M1, xp[4 * m + 2], d);
-    d = dot2(B & F::M2, xp[4 * m + 3], d);
+    d = dot2(code_pair(A, F::M1, magic), __builtin_bit_cast(half2_t, xp[4 * m + 0]), d);
+    d = dot2(code_pair(A, F::M2, magic), __builtin_bit_cast(half2_t, xp[4 * m + 1]), d);
+    d = dot2(code_pair(B, F::M1, magic), __builtin_bit_cast(half2_t, xp[4 * m + 2]), d);
+    d = dot2(code_pair(B, F::M2, magic), __builtin_bit_cast(half2_t, xp[4 * m + 3]), d);
   }
   return d;
 }
@@ -208,87 +220,159 @@ GPTQ_DEV float fold4(float v0, float v1, float v2, float v3, int lane) {
   return k;
 }
 
-template <int BITS, int NCH>
-__global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
+// ---- activation prologue ------------------------------------------------
+// Raw activations of chunk j (32 16-bit values, two per dword).
+GPTQ_DEV void load_x_raw(const GemvArgs& a, int j, bool valid, uint32_t (&v)[16]) {
+  if (!valid) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0u;
+    return;
+  }
+  const int64_t c0 = (int64_t)j * 32;
+  if (a.perm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s0 = min(max(a.perm[c0 + 2 * i], 0), a.c - 1);
+      const int s1 = min(max(a.perm[c0 + 2 * i + 1], 0), a.c - 1);
+      v[i] = (uint32_t)a.x[s0] | ((uint32_t)a.x[s1] << 16);
+    }
+  } else {
+    const u32x4* px = reinterpret_cast<const u32x4*>(a.x + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 t = px[q];
+      v[4 * q + 0] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+    }
+  }
+}
+
+// Pre-scaled fp16 pairs of one chunk, its scaled sum and exponent:
+//   e  = frexp exponent of max |x| (every |x| < 2^e);
+//   xp = pairs (x_{8m+t} 2^(16-p_lo-e), x_{8m+t+4} 2^(16-p_hi-e)), fp16;
+//   sx = sum_j x_j 2^(16-e) (fp32 sum of the unscaled values, then the exact
+//        power-of-two scaling).
+template <int BITS, bool F16X>
+GPTQ_DEV void x_prep(const uint32_t (&v)[16], uint32_t (&xp)[16], float& sx, int& ex) {
   using F = Fields<BITS>;
+  float xf[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (F16X) {
+      xf[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i] & 0xFFFFu));
+      xf[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i] >> 16));
+    } else {
+      xf[2 * i] = __uint_as_float(v[i] << 16);
+      xf[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+    }
+  }
+  float mx = 0.f, sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    mx = fmaxf(mx, fabsf(xf[i]));
+    sum += xf[i];
+  }
+  const int e1 = __builtin_amdgcn_frexp_expf(mx);
+  ex = e1;
+  sx = __builtin_ldexpf(sum, 16 - e1);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int plo = (t & 1) ? F::P2LO : F::P1LO;
+      const int phi = (t & 1) ? F::P2HI : F::P1HI;
+      const float lo = __builtin_ldexpf(xf[8 * m + t], 16 - plo - e1);
+      const float hi = __builtin_ldexpf(xf[8 * m + t + 4], 16 - phi - e1);
+      xp[4 * m + t] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+  }
+}
+
+// Template arguments: code width, chunks per lane, fp16 (else bf16)
+// activations, and whether the workgroup's waves share one activation
+// prologue through LDS (several wave groups reading the same chunks).
+template <int BITS, int NCH, bool F16X, bool SHARE>
+__global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
   __shared__ float red[2][8][4];   // [parity][wave][row]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int waves = __builtin_amdgcn_readfirstlane(blockDim.x >> 6);
   const int g = wave / a.S, sl = wave - g * a.S;
 
   // ---- chunk ownership of this lane (jc: clamped index, jv: in range)
-  int jch[kMaxNch], jc[kMaxNch], grp[kMaxNch];
+  int jc[kMaxNch], grp[kMaxNch];
   bool jv[kMaxNch];
 #pragma unroll
   for (int k = 0; k < kMaxNch; ++k) {
-    jch[k] = sl * 64 + lane + k * 64 * a.S;
-    jv[k] = jch[k] < a.nch;
-    jc[k] = jv[k] ? jch[k] : a.nch - 1;
+    const int j = sl * 64 + lane + k * 64 * a.S;
+    jv[k] = j < a.nch;
+    jc[k] = jv[k] ? j : a.nch - 1;
     grp[k] = jc[k] / a.cpg;
   }
 
-  // ---- first rows' words go out before the x prologue
   int quad = blockIdx.x * a.G + g;
   const int qstride = gridDim.x * a.G;
   const int iters = (a.nquads - (int)blockIdx.x * a.G + qstride - 1) / qstride;
   RowBuf<BITS> bufA, bufB;
-  load_quad<BITS, NCH>(a, quad, jc, grp, jv, bufA);
 
-  // ---- x prologue: pre-scaled fp16 pairs, chunk sums and exponents
-  half2_t xp[NCH][16];
+  // ---- activations go out first, then the first rows' words; the prologue
+  //      runs while the words are in flight
+  uint32_t xp[NCH][16];
   float sx[NCH];
   int ex[NCH];
+  if constexpr (SHARE) {
+    // tasks (slice, k) = t % S, t / S; wave w prepares tasks w and w + waves
+    constexpr int kMaxTasks = 2 * kMaxNch;
+    __shared__ uint32_t xl[kMaxTasks][18][64];
+    const int ntask = a.S * NCH;
+    uint32_t raw[2][16];
+    bool mine[2];
+    int tj[2];
 #pragma unroll
-  for (int k = 0; k < NCH; ++k) {
-    float xf[32];
-    if (jv[k]) {
-      const int64_t c0 = (int64_t)jch[k] * 32;
-      if (a.perm) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int src = min(max(a.perm[c0 + i], 0), a.c - 1);
-          xf[i] = x_to_f32(a.x[src], a.f16x);
-        }
-      } else {
-        const u32x4* px = reinterpret_cast<const u32x4*>(a.x + c0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 t = px[q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            xf[8 * q + 2 * e] = x_to_f32((uint16_t)(t[e] & 0xFFFFu), a.f16x);
-            xf[8 * q + 2 * e + 1] = x_to_f32((uint16_t)(t[e] >> 16), a.f16x);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) xf[i] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const int t = wave + u * waves;
+      mine[u] = t < ntask;
+      const int tsl = mine[u] ? t % a.S : 0, tk = mine[u] ? t / a.S : 0;
+      tj[u] = tsl * 64 + lane + tk * 64 * a.S;
+      load_x_raw(a, tj[u], mine[u] && tj[u] < a.nch, raw[u]);
     }
-    float mx = 0.f, sum = 0.f;
+    load_quad<BITS, NCH>(a, quad, jc, grp, jv, bufA);
+    if (iters > 1) load_quad<BITS, NCH>(a, quad + qstride, jc, grp, jv, bufB);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      mx = fmaxf(mx, fabsf(xf[i]));
-      sum += xf[i];
-    }
-    // |x| < 2^e1 for every x of the chunk (e1 = frexp exponent of the max).
-    const int e1 = __builtin_amdgcn_frexp_expf(mx);
-    ex[k] = e1;
-    sx[k] = __builtin_ldexpf(sum, -8 - e1);
+    for (int u = 0; u < 2; ++u) {
+      if (mine[u]) {
+        uint32_t p[16];
+        float s;
+        int e;
+        x_prep<BITS, F16X>(raw[u], p, s, e);
+        const int t = wave + u * waves;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int plo = (t & 1) ? F::P2LO : F::P1LO;
-        const int phi = (t & 1) ? F::P2HI : F::P1HI;
-        const float lo = __builtin_ldexpf(xf[8 * m + t], 16 - plo - e1);
-        const float hi = __builtin_ldexpf(xf[8 * m + t + 4], 16 - phi - e1);
-        xp[k][4 * m + t] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        for (int i = 0; i < 16; ++i) xl[t][i][lane] = p[i];
+        xl[t][16][lane] = __float_as_uint(s);
+        xl[t][17][lane] = (uint32_t)e;
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) {
+      const int t = k * a.S + sl;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xp[k][i] = xl[t][i][lane];
+      sx[k] = __uint_as_float(xl[t][16][lane]);
+      ex[k] = (int)xl[t][17][lane];
+    }
+  } else {
+    uint32_t raw[NCH][16];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) load_x_raw(a, sl * 64 + lane + k * 64 * a.S, jv[k], raw[k]);
+    load_quad<BITS, NCH>(a, quad, jc, grp, jv, bufA);
+    if (iters > 1) load_quad<BITS, NCH>(a, quad + qstride, jc, grp, jv, bufB);
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) x_prep<BITS, F16X>(raw[k], xp[k], sx[k], ex[k]);
   }
 
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
   auto compute = [&](const RowBuf<BITS>& b, int qd, int parity) {
     float acc[kRows];
 #pragma unroll
@@ -296,11 +380,11 @@ __global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
       float s = 0.f;
 #pragma unroll
       for (int k = 0; k < NCH; ++k) {
-        const float d = chunk_dot<BITS>(b.w[i][k], xp[k]);
+        const float d = chunk_dot<BITS>(b.w[i][k], xp[k], magic);
         const float t = __builtin_fmaf(-(float)b.z[i][k], sx[k], d);
         // scale first, then undo the chunk's power of two: no intermediate
         // overflow for activations near the top of bf16's range
-        s += __builtin_ldexpf(t * b.s[i][k], 8 + ex[k]);
+        s += __builtin_ldexpf(t * b.s[i][k], ex[k] - 16);
       }
       acc[i] = s;
     }
@@ -317,11 +401,12 @@ __global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
     if (sl == 0 && lane < kRows && qd < a.nquads && row < a.r) a.y[row] = tot;
   };
 
+  // two row quads in flight: while one is folded the next one's words land
   for (int it = 0; it < iters; it += 2) {
-    if (it + 1 < iters) load_quad<BITS, NCH>(a, quad + qstride, jc, grp, jv, bufB);
     compute(bufA, quad, 0);
     if (it + 2 < iters) load_quad<BITS, NCH>(a, quad + 2 * qstride, jc, grp, jv, bufA);
     if (it + 1 < iters) compute(bufB, quad + qstride, 1);
+    if (it + 3 < iters) load_quad<BITS, NCH>(a, quad + 3 * qstride, jc, grp, jv, bufB);
     quad += 2 * qstride;
   }
 }
@@ -385,19 +470,35 @@ void launch_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int bits,
   a.G = waves / p.S;
   a.nquads = (int)((r + kRows - 1) / kRows);
   a.f16x = x_f16;
-  const int64_t want = (a.nquads + a.G - 1) / a.G;
+  // Balanced persistent grid: at most `cap` workgroups (two of four waves or
+  // one of eight per CU), every workgroup visiting the same number of row
+  // quads give or take one.
+  const int64_t tasks = (a.nquads + a.G - 1) / a.G;
   const int64_t cap = (int64_t)device_cus() * (waves > 4 ? 1 : 2);
-  const unsigned grid = (unsigned)(want < cap ? want : cap);
+  const int64_t rounds = (tasks + cap - 1) / cap;
+  const unsigned grid = (unsigned)((tasks + rounds - 1) / rounds);
   const dim3 block(64 * waves);
+  const bool share = a.G > 1;
+#define GPTQ_GEMV_LAUNCH(B_, N_)                                                                  \
+  do {                                                                                            \
+    if (x_f16) {                                                                                  \
+      if (share) hipLaunchKernelGGL((dq_gemv_kernel<B_, N_, true, true>), dim3(grid), block, 0, s, a);   \
+      else hipLaunchKernelGGL((dq_gemv_kernel<B_, N_, true, false>), dim3(grid), block, 0, s, a);        \
+    } else {                                                                                      \
+      if (share) hipLaunchKernelGGL((dq_gemv_kernel<B_, N_, false, true>), dim3(grid), block, 0, s, a);  \
+      else hipLaunchKernelGGL((dq_gemv_kernel<B_, N_, false, false>), dim3(grid), block, 0, s, a);       \
+    }                                                                                             \
+  } while (0)
   if (bits == 4) {
-    if (p.nch_lane == 1) hipLaunchKernelGGL((dq_gemv_kernel<4, 1>), dim3(grid), block, 0, s, a);
-    else if (p.nch_lane == 2) hipLaunchKernelGGL((dq_gemv_kernel<4, 2>), dim3(grid), block, 0, s, a);
-    else hipLaunchKernelGGL((dq_gemv_kernel<4, 3>), dim3(grid), block, 0, s, a);
+    if (p.nch_lane == 1) GPTQ_GEMV_LAUNCH(4, 1);
+    else if (p.nch_lane == 2) GPTQ_GEMV_LAUNCH(4, 2);
+    else GPTQ_GEMV_LAUNCH(4, 3);
   } else {
-    if (p.nch_lane == 1) hipLaunchKernelGGL((dq_gemv_kernel<3, 1>), dim3(grid), block, 0, s, a);
-    else if (p.nch_lane == 2) hipLaunchKernelGGL((dq_gemv_kernel<3, 2>), dim3(grid), block, 0, s, a);
-    else hipLaunchKernelGGL((dq_gemv_kernel<3, 3>), dim3(grid), block, 0, s, a);
+    if (p.nch_lane == 1) GPTQ_GEMV_LAUNCH(3, 1);
+    else if (p.nch_lane == 2) GPTQ_GEMV_LAUNCH(3, 2);
+    else GPTQ_GEMV_LAUNCH(3, 3);
   }
+#undef GPTQ_GEMV_LAUNCH
 }
 
 }  // namespace gptq

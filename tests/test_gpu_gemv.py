@@ -144,6 +144,42 @@ def test_gemv_empty():
     assert torch.equal(y.cpu(), torch.zeros(5))
 
 
+def test_gemv_graph_replay():
+    """Launches captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, matches the eager result."""
+    import post_weight_quantization_23_amd as q
+    dev = "cuda"
+    layers = []
+    for i, (r, c, bits, gs, xdt) in enumerate([(300, 4096, 4, 128, "bfloat16"), (64, 11008, 3, 128, "bfloat16"),
+                                              (40, 12288, 3, 128, "float16")]):
+        codes, scales, zeros, _ = S.packed_layer_device(r, c, bits, gs, 70 + i)
+        x = torch.zeros(c, dtype=getattr(torch, xdt), device=dev)
+        layers.append(dict(packed=q.pack(codes, bits), scales=scales, zeros=zeros, x=x, bits=bits, gs=gs,
+                           y=torch.empty(r, device=dev), c=c, xdt=xdt))
+
+    def run(out_key):
+        for L in layers:
+            q.dequant_gemv(L["packed"], L["scales"], L["zeros"], L["x"], L["bits"], L["gs"], out=L[out_key])
+
+    for L in layers:
+        L["y_eager"] = torch.empty_like(L["y"])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run("y")
+    for rep in range(4):
+        for L in layers:   # eager work between replays: new activations
+            L["x"].copy_(torch.from_numpy(S.token_host(L["c"], 300 + rep, L["xdt"])).to(dev).to(L["x"].dtype))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        run("y_eager")
+        torch.cuda.synchronize()
+        for L in layers:
+            assert torch.equal(L["y"], L["y_eager"]), rep
+            assert torch.isfinite(L["y"]).all() and L["y"].abs().sum() > 0
+
+
 def test_gemv_grid_loop_sampled():
     """More row quads than the launch's workgroups hold: each wave group loops
     (odd and even trip counts); checked on sampled rows, including the last."""
