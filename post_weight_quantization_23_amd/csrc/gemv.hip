@@ -34,9 +34,10 @@
 //   * Rows are visited four at a time; the four partial sums of a wave are
 //     folded with a transposed butterfly (each exchange halves the values per
 //     lane) and, when a row's columns are split over S waves of the
-//     workgroup, summed across waves through LDS in wave order.  Two row
-//     quads are in flight per wave: the words of the next quad are loaded
-//     before the current one is used.
+//     workgroup, summed across waves through LDS in wave order once per
+//     epoch of 16 quads (the waves are not held together on every quad).
+//     Two row quads are in flight per wave: the words of the next quad are
+//     loaded before the current one is used.
 //   * act-order layers are handled by packing their codes in the order the
 //     columns were quantized (groups are then contiguous) and gathering x
 //     through that permutation once per lane.
@@ -202,19 +203,32 @@ GPTQ_DEV float chunk_dot(const Words<BITS>& v, const uint32_t (&xp)[16], uint32_
   return d;
 }
 
+// DPP lane exchange (row_mask and bank_mask all on, bound_ctrl off).
+template <int CTRL>
+GPTQ_DEV float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2, 3, 0, 1]
+constexpr int kRowRor4 = 0x124;  // row_ror:4 (rotate within 16 lanes)
+constexpr int kRowRor8 = 0x128;  // row_ror:8
+
 // Four row sums spread over the wave -> lane i (i < 4) holds row i's total.
+// Transposed butterfly: the first two exchanges (within lane quads) halve the
+// values per lane, so lane l ends with row l & 3; the rest adds the 16 lanes
+// of each residue class (rotations within rows of 16, then across rows).
 GPTQ_DEV float fold4(float v0, float v1, float v2, float v3, int lane) {
   const bool b0 = lane & 1;
   float ka = b0 ? v1 : v0, kb = b0 ? v3 : v2;
   const float sa = b0 ? v0 : v1, sb = b0 ? v2 : v3;
-  ka += __shfl_xor(sa, 1);
-  kb += __shfl_xor(sb, 1);
+  ka += dpp<kQuadXor1>(sa);
+  kb += dpp<kQuadXor1>(sb);
   const bool b1 = lane & 2;
   float k = b1 ? kb : ka;
   const float s = b1 ? ka : kb;
-  k += __shfl_xor(s, 2);
-  k += __shfl_xor(k, 4);
-  k += __shfl_xor(k, 8);
+  k += dpp<kQuadXor2>(s);
+  k += dpp<kRowRor4>(k);
+  k += dpp<kRowRor8>(k);
   k += __shfl_xor(k, 16);
   k += __shfl_xor(k, 32);
   return k;
@@ -291,8 +305,12 @@ GPTQ_DEV void x_prep(const uint32_t (&v)[16], uint32_t (&xp)[16], float& sx, int
 // activations, and whether the workgroup's waves share one activation
 // prologue through LDS (several wave groups reading the same chunks).
 template <int BITS, int NCH, bool F16X, bool SHARE>
-__global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
-  __shared__ float red[2][8][4];   // [parity][wave][row]
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NCH == 1 ? 4 : (NCH == 2 ? 3 : 2))))
+void dq_gemv_kernel(GemvArgs a) {
+  // Row sums of the column slices, kept for an epoch of row quads and summed
+  // across the slices' waves once per epoch (one pair of barriers per epoch).
+  constexpr int kEpoch = 16;
+  __shared__ float red[8][kEpoch][4];   // [wave][quad of the epoch][row]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -337,7 +355,6 @@ __global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
       load_x_raw(a, tj[u], mine[u] && tj[u] < a.nch, raw[u]);
     }
     load_quad<BITS, NCH>(a, quad, jc, grp, jv, bufA);
-    if (iters > 1) load_quad<BITS, NCH>(a, quad + qstride, jc, grp, jv, bufB);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (mine[u]) {
@@ -352,6 +369,7 @@ __global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
         xl[t][17][lane] = (uint32_t)e;
       }
     }
+    if (iters > 1) load_quad<BITS, NCH>(a, quad + qstride, jc, grp, jv, bufB);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NCH; ++k) {
@@ -373,7 +391,7 @@ __global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
 
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
-  auto compute = [&](const RowBuf<BITS>& b, int qd, int parity) {
+  auto compute = [&](const RowBuf<BITS>& b) {
     float acc[kRows];
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
@@ -388,26 +406,45 @@ __global__ __launch_bounds__(512) void dq_gemv_kernel(GemvArgs a) {
       }
       acc[i] = s;
     }
-    float tot = fold4(acc[0], acc[1], acc[2], acc[3], lane);
-    if (a.S > 1) {
-      if (lane < kRows) red[parity][wave][lane] = tot;
-      __syncthreads();
-      if (sl == 0) {
-        tot = red[parity][wave][lane & 3];
-        for (int w = 1; w < a.S; ++w) tot += red[parity][wave + w][lane & 3];
-      }
+    return fold4(acc[0], acc[1], acc[2], acc[3], lane);
+  };
+  const int quad0 = quad;
+  auto emit = [&](float tot, int it) {
+    const int qd = quad0 + it * qstride;
+    if (a.S == 1) {
+      const int row = qd * kRows + lane;
+      if (lane < kRows && qd < a.nquads && row < a.r) a.y[row] = tot;
+    } else if (lane < kRows) {
+      red[wave][it % kEpoch][lane] = tot;
     }
-    const int row = qd * kRows + lane;
-    if (sl == 0 && lane < kRows && qd < a.nquads && row < a.r) a.y[row] = tot;
+  };
+  // Sum the slices of the epoch's quads it0 .. it0 + n - 1: lane = 4 quad + row.
+  auto flush = [&](int it0, int n) {
+    __syncthreads();
+    const int e = lane >> 2, rr = lane & 3;
+    if (sl == 0 && e < n) {
+      float tot = red[wave][e][rr];
+      for (int w = 1; w < a.S; ++w) tot += red[wave + w][e][rr];
+      const int qd = quad0 + (it0 + e) * qstride;
+      const int row = qd * kRows + rr;
+      if (qd < a.nquads && row < a.r) a.y[row] = tot;
+    }
+    __syncthreads();
   };
 
   // two row quads in flight: while one is folded the next one's words land
   for (int it = 0; it < iters; it += 2) {
-    compute(bufA, quad, 0);
-    if (it + 2 < iters) load_quad<BITS, NCH>(a, quad + 2 * qstride, jc, grp, jv, bufA);
-    if (it + 1 < iters) compute(bufB, quad + qstride, 1);
-    if (it + 3 < iters) load_quad<BITS, NCH>(a, quad + 3 * qstride, jc, grp, jv, bufB);
-    quad += 2 * qstride;
+    emit(compute(bufA), it);
+    if (it + 2 < iters) load_quad<BITS, NCH>(a, quad0 + (it + 2) * qstride, jc, grp, jv, bufA);
+    if (it + 1 < iters) emit(compute(bufB), it + 1);
+    if (it + 3 < iters) load_quad<BITS, NCH>(a, quad0 + (it + 3) * qstride, jc, grp, jv, bufB);
+    if (a.S > 1) {
+      const int done = min(it + 2, iters);
+      if (done % kEpoch == 0 || done == iters) {
+        const int it0 = (done - 1) / kEpoch * kEpoch;
+        flush(it0, done - it0);
+      }
+    }
   }
 }
 
@@ -430,17 +467,23 @@ int device_cus() {
 
 }  // namespace
 
+// Launch shape from the row length: one chunk per lane when a wave covers
+// the row, else two chunks per lane over as many waves as needed (up to 8),
+// else three.  (Measured on the Llama-7B and OPT-175B layer shapes: two
+// chunks per lane balance register use against the per-row fold.)
 GemvPlan plan_gemv(int64_t c) {
   GemvPlan p{};
   const int64_t nch = c / 32;
-  p.S = 0;
-  for (int S = 1; S <= 8; S *= 2) {
-    if ((nch + 64 * S - 1) / (64 * S) <= kMaxNch) {
-      p.S = S;
-      break;
-    }
+  if (nch <= 64) {
+    p.S = 1;
+    p.nch_lane = 1;
+  } else if (nch <= 8 * 64 * 2) {
+    p.S = (int)((nch + 127) / 128);
+    p.nch_lane = 2;
+  } else if (nch <= 8 * 64 * kMaxNch) {
+    p.S = (int)((nch + 64 * kMaxNch - 1) / (64 * kMaxNch));
+    p.nch_lane = kMaxNch;
   }
-  if (p.S) p.nch_lane = (int)((nch + 64 * p.S - 1) / (64 * p.S));
   return p;
 }
 
@@ -466,15 +509,19 @@ void launch_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int bits,
   a.nch = (int)(c / 32);
   a.cpg = (groupsize > 0 && groupsize < c) ? (int)(groupsize / 32) : a.nch;
   a.S = p.S;
-  const int waves = p.S > 4 ? p.S : 4;
-  a.G = waves / p.S;
+  a.G = p.S >= 4 ? 1 : 4 / p.S;
+  const int waves = a.S * a.G;
   a.nquads = (int)((r + kRows - 1) / kRows);
   a.f16x = x_f16;
-  // Balanced persistent grid: at most `cap` workgroups (two of four waves or
-  // one of eight per CU), every workgroup visiting the same number of row
-  // quads give or take one.
+  // Balanced persistent grid: at most `cap` workgroups (as many as the
+  // register budget keeps resident on every CU at once), every workgroup
+  // visiting the same number of row quads give or take one.  Waves per SIMD
+  // the register budget allows:
+  // ~100 VGPRs with one chunk per lane, ~165 with two, ~235 with three.
   const int64_t tasks = (a.nquads + a.G - 1) / a.G;
-  const int64_t cap = (int64_t)device_cus() * (waves > 4 ? 1 : 2);
+  const int per_simd = p.nch_lane == 1 ? 4 : (p.nch_lane == 2 ? 3 : 2);
+  const int per_cu = (4 * per_simd) / waves > 0 ? (4 * per_simd) / waves : 1;
+  const int64_t cap = (int64_t)device_cus() * per_cu;
   const int64_t rounds = (tasks + cap - 1) / cap;
   const unsigned grid = (unsigned)((tasks + rounds - 1) / rounds);
   const dim3 block(64 * waves);

@@ -77,13 +77,16 @@ def _run(codes, scales, zeros, perm, x, bits, groupsize, xdtype):
 CASES = [
     (37, 256, 4, 128, "bfloat16", False),     # S 1, 1 chunk, ragged lanes and rows
     (37, 256, 3, 128, "float16", True),
-    (130, 2048, 4, -1, "float16", False),     # one ruler per row
+    (130, 2048, 4, -1, "float16", False),     # S 1, 1 chunk; one ruler per row
     (130, 2048, 3, 32, "bfloat16", False),    # one group per chunk
     (64, 4096, 4, 128, "bfloat16", True),     # S 1, 2 chunks
     (64, 4096, 3, 128, "bfloat16", False),
-    (9, 11008, 3, 128, "bfloat16", True),     # S 2, 3 chunks, ragged chunks
+    (9, 11008, 3, 128, "bfloat16", True),     # S 3, 2 chunks, ragged chunks
     (9, 11008, 4, 128, "float16", False),
-    (6, 12288, 3, 128, "float16", False),     # S 2, 3 chunks
+    (6, 12288, 3, 128, "float16", False),     # S 3, 2 chunks
+    (7, 20480, 4, 128, "bfloat16", False),    # S 5, 2 chunks
+    (6, 28672, 3, 128, "float16", True),      # S 7, 2 chunks
+    (3, 32800, 4, -1, "bfloat16", False),     # S 6, 3 chunks, ragged
     (5, 49152, 3, 128, "float16", False),     # S 8, 3 chunks
     (5, 49152, 4, -1, "bfloat16", True),
     (3, 32, 4, -1, "bfloat16", False),        # a single chunk
