@@ -46,6 +46,8 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_syrk16_{workload}.json")
 SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "syrk.hip")
+GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_{workload}.json")
+GEMV_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "gemv.hip")
 
 
 def log(*a):
@@ -57,15 +59,15 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(workload: str):
-    """HBM bytes per SYRK launch from committed PMC counters, or None when the
-    kernel source changed since they were taken."""
-    path = TRAFFIC_FILE.format(workload=workload)
+def load_traffic(workload: str, path_fmt: str = TRAFFIC_FILE, source: str = SYRK_SOURCE):
+    """HBM bytes per launch of the dominant kernel from committed PMC counters,
+    or None when the kernel source changed since they were taken."""
+    path = path_fmt.format(workload=workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_sha256") != source_hash(SYRK_SOURCE):
+    if t.get("source_sha256") != source_hash(source):
         return None
     return t.get("bytes_per_launch")
 
@@ -320,7 +322,7 @@ def bench_gemv(args) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None,
+            "traffic": load_traffic(f"{args.gemv_model}_decode_token_{bits}bit_g{gs}", GEMV_TRAFFIC_FILE, GEMV_SOURCE),
             "algorithmic_bytes_per_launch": b_launch,
             "us_per_launch": us_launch,
         },
