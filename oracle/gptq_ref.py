@@ -80,6 +80,9 @@ __all__ = [
     "pack_codes",
     "unpack_codes",
     "dequant_gemv",
+    "hadamard",
+    "default_hadamard_block",
+    "hadamard_rotate",
 ]
 
 
@@ -528,4 +531,43 @@ def dequant_gemv(words, bits: int, c: int, scales, zeros, g_idx, x) -> np.ndarra
     g = np.asarray(g_idx, np.int64)
     w_hat = dequantize(codes, np.asarray(scales)[:, g], np.asarray(zeros, F64)[:, g])
     return w_hat @ np.asarray(x, F64)
+
+
+# ---------------------------------------------------------------------------
+# Hadamard pre-rotation -- "Post-Training Quantization: Calibration, GPTQ and
+# Why Rotations Help", sections "Rotations: making outliers disappear" and
+# "Why do Hadamard rotations help quantization?": a Hadamard matrix (entries
+# +-1, mutually perpendicular rows), scaled to a rotation Q, spreads a lone
+# large activation over all entries; rotating the layer's inputs by Q and its
+# weights by Q^{-1} = Q^T leaves the product unchanged: (W Q^T)(Q x) = W x.
+# Readings: the Sylvester construction (H_1 = [1], H_2k = [[H, H], [H, -H]]),
+# Q = H / sqrt(b); a width d that is not a power of two is rotated block-wise,
+# Q = blockdiag(H_b / sqrt(b)) with b the largest power of two dividing d.
+# Rows of X (token-major) and of W (one row per output) are both rotated along
+# their last axis: x_t -> Q x_t and w_i -> Q w_i (Q is symmetric).
+# ---------------------------------------------------------------------------
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("n must be a power of two")
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def default_hadamard_block(d: int) -> int:
+    """Largest power of two dividing d."""
+    return d & -d
+
+
+def hadamard_rotate(A, block: int | None = None) -> np.ndarray:
+    """Each row of A [m, d] times blockdiag(H_b / sqrt(b)), in float64."""
+    A = np.asarray(A, F64)
+    m, d = A.shape
+    b = default_hadamard_block(d) if not block else int(block)
+    if d % b:
+        raise ValueError("block must divide d")
+    Q = hadamard(b) / np.sqrt(b)
+    return (A.reshape(m, d // b, b) @ Q.T).reshape(m, d)
 

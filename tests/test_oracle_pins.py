@@ -467,3 +467,54 @@ def test_dequant_gemv_matches_the_quantizers_w_hat(bits, groupsize, act_order):
     y = ref.dequant_gemv(words, bits, c, out["scales"], out["zeros"], out["g_idx"], x)
     np.testing.assert_allclose(y, out["w_hat"] @ x, rtol=1e-12, atol=1e-15)
 
+
+# --- Hadamard pre-rotation ---
+def test_hadamard_small_orders_written_out():
+    np.testing.assert_array_equal(ref.hadamard(1), [[1]])
+    np.testing.assert_array_equal(ref.hadamard(2), [[1, 1], [1, -1]])
+    np.testing.assert_array_equal(ref.hadamard(4), [[1, 1, 1, 1], [1, -1, 1, -1], [1, 1, -1, -1], [1, -1, -1, 1]])
+
+
+@pytest.mark.parametrize("n", [8, 64, 256])
+def test_hadamard_rows_are_perpendicular_and_pm1(n):
+    H = ref.hadamard(n)
+    assert set(np.unique(H)) == {-1.0, 1.0}
+    np.testing.assert_array_equal(H @ H.T, n * np.eye(n))
+    np.testing.assert_array_equal(H, H.T)
+
+
+def test_rotation_leaves_the_layer_product_unchanged():
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((5, 96))       # 96 = 3 * 32: block 32
+    x = rng.standard_normal(96)
+    Wr = ref.hadamard_rotate(W)
+    xr = ref.hadamard_rotate(x[None])[0]
+    np.testing.assert_allclose(Wr @ xr, W @ x, rtol=1e-12, atol=1e-12)
+    # rotation preserves each row's norm and the Hessian's eigen-structure: H_r = Q H Q^T
+    np.testing.assert_allclose(np.linalg.norm(Wr, axis=1), np.linalg.norm(W, axis=1), rtol=1e-13)
+    X = rng.standard_normal((40, 96))
+    Xr = ref.hadamard_rotate(X)
+    np.testing.assert_allclose(np.linalg.eigvalsh(ref.hessian(Xr)), np.linalg.eigvalsh(ref.hessian(X)),
+                               rtol=1e-10, atol=1e-9)
+
+
+def test_rotation_spreads_a_lone_outlier():
+    x = np.zeros((1, 64))
+    x[0, 17] = 100.0
+    y = ref.hadamard_rotate(x)
+    np.testing.assert_allclose(np.abs(y), 100.0 / 8.0)     # every entry +-100 / sqrt(64)
+    assert np.max(np.abs(y)) < np.max(np.abs(x)) / 7.9
+
+
+def test_rotation_blocks_and_default_block():
+    assert ref.default_hadamard_block(4096) == 4096
+    assert ref.default_hadamard_block(11008) == 256
+    assert ref.default_hadamard_block(12288) == 4096
+    rng = np.random.default_rng(2)
+    A = rng.standard_normal((3, 48))
+    B = ref.hadamard_rotate(A, 16)
+    for k in range(3):                    # block-diagonal: each 16-block on its own
+        np.testing.assert_allclose(B[:, 16 * k:16 * (k + 1)], A[:, 16 * k:16 * (k + 1)] @ ref.hadamard(16) / 4.0,
+                                   rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(ref.hadamard_rotate(B, 16), A, rtol=1e-12, atol=1e-12)   # Q^2 = I (symmetric, orthogonal)
+
