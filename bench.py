@@ -15,6 +15,7 @@ oracle timed on a bounded sample of the same workload.
                     [--no-cpu-baseline]
     python bench.py --copy-probe      # plain copy of known size (PMC calibration)
     python bench.py --gemv [--gemv-model llama7b|opt175b] [--steps K] [--warmup W]
+    python bench.py --hadamard [--workload NAME] [--steps K] [--warmup W]
 
 --gemv measures the dequantizing matrix-vector product over packed layers
 instead: one step = one generated token (batch 1) through every linear layer
@@ -337,6 +338,64 @@ def bench_gemv(args) -> int:
     return 0
 
 
+def bench_hadamard(args) -> int:
+    """Hadamard pre-rotation of the workload's calibration activations (one
+    step = the whole X, rotated into a second buffer of the same dtype)."""
+    import numpy as np
+    import torch
+
+    from post_weight_quantization_23_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_23_amd import build as b
+        b.build()
+    import post_weight_quantization_23_amd as q
+    from synth import inputs as S
+
+    w = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    _, X = S.workload_device(w, device=dev)
+    Xr = torch.empty_like(X)
+    block = min(X.shape[1] & -X.shape[1], 8192)
+    for _ in range(max(1, args.warmup)):
+        q.hadamard_rotate(X, out=Xr)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        q.hadamard_rotate(X, out=Xr)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 2 * X.numel() * X.element_size()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": f"Hadamard pre-rotation of the calibration activations ({w.tokens}x{w.cols} {w.x_dtype}, "
+                  f"block {block}): GB/s",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 butterflies, " + w.x_dtype + " in/out", "data": "synthetic (the workload's activations)",
+        "config": {"workload": w.name + "_hadamard", "rows": w.tokens, "cols": w.cols, "block": block},
+        "roofline": {"kernel": f"fwht_kernel<{block.bit_length() - 1},*> (HIP events around back-to-back launches)",
+                     "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gptq_ref as ref
+        sample = 8192
+        A = X[:sample].float().cpu().numpy()
+        t0 = time.perf_counter()
+        ref.hadamard_rotate(A, block)
+        t = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": 2 * sample * w.cols * X.element_size() / t / 1e9, "unit": "GB/s",
+                               "cores": int(torch.get_num_threads()), "kind": "oracle",
+                               "sample": f"{sample} of {w.tokens} rows ({t:.2f} s), float64 matrix product per block"}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +406,7 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--gemv", action="store_true")
     ap.add_argument("--gemv-model", default="llama7b", choices=sorted(GEMV_MODELS))
+    ap.add_argument("--hadamard", action="store_true")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -361,6 +421,8 @@ def main(argv=None) -> int:
         return 0
     if args.gemv:
         return bench_gemv(args)
+    if args.hadamard:
+        return bench_hadamard(args)
 
     from post_weight_quantization_23_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):

@@ -223,6 +223,33 @@ gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int 
                               int64_t ld_groups, int64_t groupsize, const int32_t* col_perm,
                               const void* x, gptq_dtype xt, float* y, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Hadamard pre-rotation of rows.  Page: "Post-Training Quantization:
+ * Calibration, GPTQ and Why Rotations Help", sections "Rotations: making
+ * outliers disappear" and "Why do Hadamard rotations help quantization?"
+ * (a Hadamard matrix scaled to a rotation spreads outliers; rotating a
+ * layer's inputs and applying the inverse rotation to its weights leaves the
+ * product unchanged).
+ *
+ *   out[i, :] = A[i, :] * blockdiag(H_b / sqrt(b), ..., H_b / sqrt(b))
+ *
+ * with H_b Sylvester's Hadamard matrix of order b (symmetric; the rotation is
+ * its own inverse).  Rotate the calibration activations X (token-major, one
+ * token per row) and the weights W (one output per row) with the same b: then
+ * W_rot x_rot = W x for every input, and H of the rotated X is Q H Q^T.
+ *
+ * A    : rows x d, row stride lda, dtype at (f32 / bf16 / f16).
+ * block: b, a power of two in 32 .. 8192 dividing d; <= 0 picks the largest
+ *        power of two dividing d, capped at 8192 (a width that is not a power
+ *        of two is rotated block-wise).
+ * out  : rows x d, row stride ldo, dtype ot; fp32 arithmetic, rounded once
+ *        (round-to-nearest-even) to ot.  out may be A itself (same dtype and
+ *        stride); any other overlap is GPTQ_EINVAL.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int64_t d,
+                                 int64_t lda, int64_t block, void* out, gptq_dtype ot,
+                                 int64_t ldo, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* gptq_status_string(gptq_status s);
 /* Detail of the last failure on the calling thread (thread-local storage). */

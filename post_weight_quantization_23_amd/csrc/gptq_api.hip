@@ -232,4 +232,33 @@ gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int 
   return check_launch(fn);
 }
 
+// ------------------------------------------------------------------ Hadamard pre-rotation
+gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int64_t d, int64_t lda,
+                                 int64_t block, void* out, gptq_dtype ot, int64_t ldo, void* stream) {
+  const char* fn = "gptq_hadamard_rotate";
+  if (rows < 0 || d < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (!valid_dtype(at) || !valid_dtype(ot)) return fail(GPTQ_EDTYPE, fn, "at and ot must be gptq_dtype values");
+  if (block <= 0 && d > 0) {
+    block = d & -d;
+    if (block > 8192) block = 8192;
+  }
+  if (d > 0 && (block < 32 || block > 8192 || (block & (block - 1)) != 0))
+    return fail(GPTQ_EUNSUPPORTED, fn, "block must be a power of two in 32 .. 8192");
+  if (d > 0 && d % block != 0) return fail(GPTQ_ESHAPE, fn, "block must divide d");
+  if (rows == 0 || d == 0) return ok();
+  if (lda < d || ldo < d) return fail(GPTQ_ESHAPE, fn, "lda and ldo must be >= d");
+  if ((rows * (d / block)) >= (int64_t)INT_MAX) return fail(GPTQ_EUNSUPPORTED, fn, "too many blocks");
+  if (!A || !out) return fail(GPTQ_EINVAL, fn, "A or out is NULL");
+  if (!aligned(A, elem_size(at)) || !aligned(out, elem_size(ot))) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
+  const char* a0 = static_cast<const char*>(A);
+  const char* a1 = a0 + ((rows - 1) * lda + d) * (int64_t)elem_size(at);
+  const char* o0 = static_cast<const char*>(out);
+  const char* o1 = o0 + ((rows - 1) * ldo + d) * (int64_t)elem_size(ot);
+  const bool overlap = a0 < o1 && o0 < a1;
+  if (overlap && !(A == out && at == ot && lda == ldo))
+    return fail(GPTQ_EINVAL, fn, "out overlaps A (only exact in-place use is allowed)");
+  gptq::launch_hadamard(A, (int)at, lda, rows, d, block, out, (int)ot, ldo, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
 }  // extern "C"

@@ -72,6 +72,11 @@ void launch_quantize(const QuantArgs& a, hipStream_t s);
 void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, const int32_t* perm,
                  uint32_t* packed, int64_t ld_words, hipStream_t s);
 
+// --- Hadamard pre-rotation (hadamard.hip) ---
+// at / ot: 0 f32, 1 bf16, 2 f16; block a power of two in 32 .. 8192 dividing d.
+void launch_hadamard(const void* A, int at, int64_t lda, int64_t rows, int64_t d, int64_t block, void* out,
+                     int ot, int64_t ldo, hipStream_t s);
+
 // --- Dequantize-on-the-fly product (gemv.hip) ---
 struct GemvPlan {
   int S;         // waves sharing one row's columns (0: c too large)

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import GPTQ_BF16, GPTQ_F16, GPTQ_F32, GPTQError
 
-__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "Workspace",
+__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "hadamard_rotate", "Workspace",
            "NotPositiveDefinite", "GPTQError"]
 
 _DT = {torch.float32: GPTQ_F32, torch.bfloat16: GPTQ_BF16, torch.float16: GPTQ_F16}
@@ -210,3 +210,22 @@ def dequant_gemv(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor
     _lib.call("gptq_dequant_gemv", _ptr(packed), r, c, int(bits), packed.stride(0), _ptr(scales), _ptr(zeros),
               scales.stride(0), int(groupsize), _ptr(perm), _ptr(x), _DT[x.dtype], _ptr(out), _stream())
     return out
+
+
+def hadamard_rotate(A: torch.Tensor, block: int = 0, out: torch.Tensor | None = None,
+                    out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """Rows of A [m, d] times blockdiag(H_b / sqrt(b)) (Sylvester H_b); block <= 0
+    picks the largest power of two dividing d (at most 8192).  out may be A."""
+    _need(A, "A", None, 2)
+    if A.dtype not in _DT or A.stride(1) != 1:
+        raise ValueError("A must be f32/bf16/f16 with contiguous rows")
+    if out is None:
+        out = torch.empty(A.shape, dtype=out_dtype or A.dtype, device=A.device)
+    _need(out, "out", None, 2, A.device)
+    if out.shape != A.shape or out.dtype not in _DT or out.stride(1) != 1:
+        raise ValueError("out must match A's shape with contiguous rows")
+    m, d = A.shape
+    _lib.call("gptq_hadamard_rotate", _ptr(A), _DT[A.dtype], m, d, A.stride(0), int(block), _ptr(out),
+              _DT[out.dtype], out.stride(0), _stream())
+    return out
+

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_symbols_are_exported(lib):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -149,6 +149,26 @@ def test_dequant_gemv_argument_errors(lib):
     assert g(bits=3, ldw=24, packed=C.c_void_p(0x10004), y=C.c_void_p(0x10002)) == 4
     assert g(x=C.c_void_p(0x10002)) == 4       # x 16-byte aligned without perm
     assert g(perm=C.c_void_p(0x10002)) == 4
+
+
+def test_hadamard_argument_errors(lib):
+    f = "gptq_hadamard_rotate"
+    A, O = ALIGNED, C.c_void_p(0x40000000)
+
+    def h(a=A, at=1, rows=4, d=4096, lda=4096, block=0, out=O, ot=1, ldo=4096):
+        return _st(lib, f, a, at, rows, d, lda, block, out, ot, ldo, None)
+
+    assert h(rows=0) == 0 and h(d=0) == 0
+    assert h(rows=-1) == 1
+    assert h(at=5) == 2 and h(ot=-1) == 2
+    assert h(block=16) == 5 and h(block=96) == 5 and h(block=16384) == 5
+    assert h(d=4000, lda=4000, ldo=4000, block=64) == 3           # 64 does not divide 4000
+    assert h(d=48, lda=48, ldo=48) == 5                           # default block 16 is too small
+    assert h(lda=100) == 3 and h(ldo=100) == 3
+    assert h(a=None) == 1 and h(out=None) == 1
+    assert h(a=C.c_void_p(0x10001)) == 4
+    assert h(out=C.c_void_p(0x10000 + 2 * 4096)) == 1             # overlaps A without being A
+    assert h(out=A, ot=0) == 1                                     # in place needs the same dtype
 
 
 def test_python_binding_rejects_cpu_tensors():

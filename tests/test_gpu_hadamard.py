@@ -1,0 +1,141 @@
+"""Parity of the Hadamard pre-rotation (gptq_hadamard_rotate) with the float64
+oracle, through the C ABI.
+
+Bar, from the arithmetic: the kernel adds in fp32 through log2(b) butterfly
+stages and scales once, so an fp32 result is within
+    err = (log2(b) + 2) * 2^-24 * sum_{j in the block} |a_j| / sqrt(b)
+of the exact value.  A bf16 / fp16 result is that fp32 value rounded once
+(round-to-nearest-even): it may differ from the correctly rounded exact value
+only where the exact value lies within err of a rounding midpoint, so the test
+asserts |out - exact| <= ulp(out) / 2 + err element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import gptq_ref as ref
+from synth import inputs as S
+
+pytestmark = pytest.mark.gpu
+
+DT = {"float32": torch.float32, "bfloat16": torch.bfloat16, "float16": torch.float16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import post_weight_quantization_23_amd as q  # noqa: F401  (loads the library, raises if missing)
+    yield
+    torch.cuda.empty_cache()
+
+
+def _ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    mant = {"float32": 23, "bfloat16": 7, "float16": 10}[dtype]
+    emin = {"float32": -126, "bfloat16": -126, "float16": -14}[dtype]
+    e = np.floor(np.log2(np.maximum(np.abs(v), 1e-300)))
+    return np.exp2(np.maximum(e, emin) - mant)
+
+
+def _check(out: np.ndarray, A: np.ndarray, block: int, out_dtype: str):
+    m, d = A.shape
+    b = block or min(ref.default_hadamard_block(d), 8192)
+    exact = ref.hadamard_rotate(A, b)
+    mass = np.abs(A).reshape(m, d // b, b).sum(axis=2, keepdims=True) / np.sqrt(b)
+    err = (np.log2(b) + 2) * 2.0 ** -24 * np.broadcast_to(mass, (m, d // b, b)).reshape(m, d)
+    tol = err if out_dtype == "float32" else err + 0.5 * _ulp(out, out_dtype)
+    dev = np.abs(out.astype(np.float64) - exact)
+    worst = float(np.max(dev / np.maximum(tol, 1e-300))) if dev.size else 0.0
+    print(f"  max |out - exact| / allowed = {worst:.3g}", flush=True)
+    assert np.all(dev <= tol), worst
+
+
+CASES = [
+    # rows, d, block (0: default), input dtype, output dtype
+    (3, 4096, 0, "bfloat16", "float32"),    # b 4096: bits 8..11 in registers, two LDS passes
+    (5, 11008, 0, "bfloat16", "bfloat16"),  # b 256, 16 blocks per tile across rows
+    (7, 12288, 0, "float16", "float16"),    # b 4096, three blocks per row
+    (2, 49152, 0, "float16", "float32"),    # b 8192 (cap), 32 elements per thread
+    (33, 256, 32, "float32", "float32"),    # smallest block, tile spans 16 rows, ragged last tile
+    (4, 1024, 64, "float32", "bfloat16"),
+    (9, 8192, 8192, "bfloat16", "float32"),
+    (1, 2048, 128, "bfloat16", "bfloat16"),
+    (17, 640, 128, "float32", "float16"),   # 640 = 5 x 128
+    (6, 1536, 512, "bfloat16", "float32"),  # b 512: one register stage, blocks of a tile in k
+    (3, 6144, 2048, "float16", "bfloat16"),
+]
+
+
+@pytest.mark.parametrize("rows,d,block,idt,odt", CASES)
+def test_rotation_matches_oracle(rows, d, block, idt, odt):
+    import post_weight_quantization_23_amd as q
+    print(f"\n[hadamard] {rows}x{d} block={block} {idt}->{odt}", flush=True)
+    A = S.activations_host(rows, d, "t4", max(1, d // 200), 30.0, wid=60 + rows, dtype=idt)
+    Ad = torch.from_numpy(A).cuda().to(DT[idt])
+    out = q.hadamard_rotate(Ad, block, out_dtype=DT[odt])
+    torch.cuda.synchronize()
+    _check(out.float().cpu().numpy(), A, block, odt)
+
+
+def test_rotation_in_place_and_strided():
+    import post_weight_quantization_23_amd as q
+    rows, d = 6, 4096
+    A = S.activations_host(rows, d, "t4", 20, 30.0, wid=71, dtype="bfloat16")
+    wide = torch.zeros((rows, d + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, 32:32 + d] = torch.from_numpy(A).cuda().to(torch.bfloat16)
+    view = wide[:, 32:32 + d]                    # row stride d + 64, offset 64 bytes
+    q.hadamard_rotate(view, 0, out=view)         # in place
+    torch.cuda.synchronize()
+    _check(view.float().cpu().numpy(), A, 0, "bfloat16")
+    assert torch.count_nonzero(wide[:, :32]) == 0 and torch.count_nonzero(wide[:, 32 + d:]) == 0
+
+
+@pytest.mark.parametrize("d,block,idt,odt", [(4096, 0, "bfloat16", "bfloat16"), (768, 256, "float16", "float32"),
+                                             (8192, 8192, "float32", "bfloat16"), (96, 32, "bfloat16", "float16")])
+def test_rotation_unaligned_rows(d, block, idt, odt):
+    """Rows that do not start on 16 bytes take the element-wise path."""
+    import post_weight_quantization_23_amd as q
+    rows = 5
+    print(f"\n[hadamard unaligned] {rows}x{d} block={block} {idt}->{odt}", flush=True)
+    A = S.activations_host(rows, d, "t4", max(1, d // 200), 30.0, wid=80 + d % 7, dtype=idt)
+    wide = torch.zeros((rows, d + 3), dtype=DT[idt], device="cuda")
+    wide[:, 1:1 + d] = torch.from_numpy(A).cuda().to(DT[idt])
+    out = q.hadamard_rotate(wide[:, 1:1 + d], block, out_dtype=DT[odt])
+    torch.cuda.synchronize()
+    _check(out.float().cpu().numpy(), A, block, odt)
+
+
+def test_rotation_preserves_the_layer_product():
+    """W_rot x_rot = W x: weights rotated (fp32 out) and the activation rotated
+    with the same block, on the GPU; compared with the unrotated product."""
+    import post_weight_quantization_23_amd as q
+    r, d = 64, 11008
+    W = S.weights_host(r, d, wid=72, dtype="float32")
+    x = S.activations_host(1, d, "t4", 50, 30.0, wid=73, dtype="float32")
+    Wr = q.hadamard_rotate(torch.from_numpy(W).cuda()).cpu().numpy().astype(np.float64)
+    xr = q.hadamard_rotate(torch.from_numpy(x).cuda()).cpu().numpy().astype(np.float64)
+    y, yr = W.astype(np.float64) @ x[0].astype(np.float64), Wr @ xr[0]
+    scale = np.abs(W).astype(np.float64) @ np.abs(x[0]).astype(np.float64)
+    assert np.max(np.abs(yr - y) / scale) < 1e-5
+    # and the lone outliers are spread: the rotated activation's peak is far lower
+    assert np.abs(xr).max() < 0.2 * np.abs(x).max()
+
+
+def test_rotation_empty():
+    import post_weight_quantization_23_amd as q
+    out = q.hadamard_rotate(torch.zeros((0, 4096), dtype=torch.bfloat16, device="cuda"))
+    assert out.shape == (0, 4096)
+
+
+def test_rotation_full_size_x_sampled():
+    """The benchmark's activation matrix (262144 x 4096 bf16, rotated into a
+    second bf16 buffer), checked on sampled rows."""
+    import post_weight_quantization_23_amd as q
+    w = S.WORKLOADS["llama7b_attn_4096x4096"]
+    print(f"\n[hadamard full] X {w.tokens}x{w.cols} {w.x_dtype}", flush=True)
+    _, X = S.workload_device(w, device="cuda")
+    Xr = q.hadamard_rotate(X)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, w.tokens - 1], rng.choice(w.tokens, 29, replace=False)]))
+    rd = torch.from_numpy(rows).cuda()
+    _check(Xr[rd].float().cpu().numpy(), X[rd].float().cpu().numpy(), 0, w.x_dtype)
