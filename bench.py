@@ -49,6 +49,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_syrk16_{workload}.json")
 SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "syrk.hip")
 GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_{workload}.json")
 GEMV_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "gemv.hip")
+HADAMARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hadamard_{workload}.json")
+HADAMARD_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "hadamard.hip")
 
 
 def log(*a):
@@ -378,7 +380,9 @@ def bench_hadamard(args) -> int:
         "config": {"workload": w.name + "_hadamard", "rows": w.tokens, "cols": w.cols, "block": block},
         "roofline": {"kernel": f"fwht_kernel<{block.bit_length() - 1},*> (HIP events around back-to-back launches)",
                      "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+                     "frac": gbs / PEAK_HBM_GBS,
+                     "traffic": load_traffic(w.name + "_hadamard", HADAMARD_TRAFFIC_FILE, HADAMARD_SOURCE),
+                     "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
         from oracle import gptq_ref as ref
