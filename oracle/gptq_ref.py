@@ -83,6 +83,10 @@ __all__ = [
     "hadamard",
     "default_hadamard_block",
     "hadamard_rotate",
+    "round16",
+    "silu",
+    "linear_forward",
+    "quantize_mlp_stack",
 ]
 
 
@@ -570,4 +574,68 @@ def hadamard_rotate(A, block: int | None = None) -> np.ndarray:
         raise ValueError("block must divide d")
     Q = hadamard(b) / np.sqrt(b)
     return (A.reshape(m, d // b, b) @ Q.T).reshape(m, d)
+
+
+# ---------------------------------------------------------------------------
+# Layer by layer -- "What is GPTQ" (queryfeedz glossary), section "How it
+# works": layers are quantized one at a time and each next layer is
+# calibrated on the quantized outputs of the previous one; "Post-Training
+# Quantization: Calibration, GPTQ and Why Rotations Help", section
+# "Calibration: letting data pick the rounding": the layer's calibration
+# inputs are what the (already quantized) model feeds it.
+# Readings: the forward pass runs in the model's 16-bit type -- the
+# dequantized weights and every layer output are rounded once to it
+# (round-to-nearest-even); a gated MLP block is down(silu(gate(x)) * up(x));
+# linears that read the same input (gate and up) share one Hessian.
+# ---------------------------------------------------------------------------
+_MANT = {"bfloat16": 7, "float16": 10, "float32": 23}
+_EMIN = {"bfloat16": -126, "float16": -14, "float32": -126}
+_MAX = {"bfloat16": (2 - 2.0 ** -7) * 2.0 ** 127, "float16": 65504.0, "float32": float(np.finfo(np.float32).max)}
+
+
+def round16(x, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest value of `dtype` (ties to even),
+    in one step: q = rint(x / ulp) * ulp with ulp the spacing at |x|."""
+    x = np.asarray(x, F64)
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    ulp = np.exp2(np.maximum(e, _EMIN[dtype]) - _MANT[dtype])
+    y = np.rint(x / ulp) * ulp
+    big = np.abs(y) > _MAX[dtype]
+    return np.where(big, np.copysign(np.inf, y), y)
+
+
+def silu(g):
+    g = np.asarray(g, F64)
+    return g / (1.0 + np.exp(-g))
+
+
+def linear_forward(X, W_hat, dtype: str, gate=None, out_dtype: str | None = None) -> np.ndarray:
+    """X W_hat^T with W_hat rounded once to the 16-bit `dtype`, float64 sums;
+    with `gate`: silu(gate) * round(X W_hat^T).  Rounded to out_dtype if given."""
+    Wr = round16(W_hat, dtype)
+    acc = np.asarray(X, F64) @ Wr.T
+    y = acc if gate is None else silu(gate) * round16(acc, dtype)
+    return round16(y, out_dtype) if out_dtype else y
+
+
+def quantize_mlp_stack(X0, blocks, bits: int, groupsize: int = -1, percdamp: float = 0.01,
+                       act_order: bool = False, dtype: str = "bfloat16"):
+    """GPTQ over a stack of gated MLP blocks (W_gate [h, d], W_up [h, d],
+    W_down [d, h]), one layer at a time, each calibrated on the quantized
+    outputs of the layers before it.  Returns (records, final output)."""
+    X = np.asarray(X0, F64)
+    records = []
+    for Wg, Wu, Wd in blocks:
+        H = hessian(X)                                          # shared by gate and up
+        qg = gptq_quantize(Wg, H, bits, groupsize, percdamp, act_order)
+        qu = gptq_quantize(Wu, H, bits, groupsize, percdamp, act_order)
+        G = linear_forward(X, qg["w_hat"], dtype, out_dtype=dtype)
+        Z = linear_forward(X, qu["w_hat"], dtype, gate=G, out_dtype=dtype)
+        H2 = hessian(Z)
+        qd = gptq_quantize(Wd, H2, bits, groupsize, percdamp, act_order)
+        Xn = linear_forward(Z, qd["w_hat"], dtype, out_dtype=dtype)
+        records.append({"X": X, "H": H, "gate": qg, "up": qu, "G": G, "Z": Z, "H2": H2, "down": qd})
+        X = Xn
+    return records, X
 

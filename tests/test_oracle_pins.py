@@ -518,3 +518,72 @@ def test_rotation_blocks_and_default_block():
                                    rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(ref.hadamard_rotate(B, 16), A, rtol=1e-12, atol=1e-12)   # Q^2 = I (symmetric, orthogonal)
 
+
+# --- layer-by-layer pass ---
+def test_round16_agrees_with_torch_single_rounding():
+    import torch
+    rng = np.random.default_rng(11)
+    x32 = (rng.standard_normal(20000) * np.exp(rng.uniform(-30, 30, 20000))).astype(np.float32)
+    for dt, tdt in (("bfloat16", torch.bfloat16), ("float16", torch.float16)):
+        want = torch.from_numpy(x32).to(tdt).to(torch.float64).numpy()
+        got = ref.round16(x32.astype(np.float64), dt)
+        np.testing.assert_array_equal(got, want)
+    # ties to even, written out
+    assert ref.round16(1 + 2.0 ** -8, "bfloat16") == 1.0
+    assert ref.round16(1 + 3 * 2.0 ** -8, "bfloat16") == 1 + 2.0 ** -6
+    assert ref.round16(2.0 ** -25, "float16") == 0.0 and ref.round16(3 * 2.0 ** -25, "float16") == 2.0 ** -23
+
+
+def test_linear_forward_closed_form():
+    X = np.array([[1.0, 2.0], [-1.0, 0.5]])
+    W = np.array([[0.5, 0.25], [1.0, -1.0], [2.0, 0.0]])      # all exact in bf16
+    np.testing.assert_array_equal(ref.linear_forward(X, W, "bfloat16"), [[1.0, -1.0, 2.0], [-0.375, -1.5, -2.0]])
+    G = np.array([[0.0, 1.0, -2.0], [3.0, 0.0, 1.0]])
+    s = lambda g: g / (1 + np.exp(-g))
+    want = np.array([[0.0, s(1.0) * -1.0, s(-2.0) * 2.0], [s(3.0) * -0.375, 0.0, s(1.0) * -2.0]])
+    np.testing.assert_allclose(ref.linear_forward(X, W, "bfloat16", gate=G), want, rtol=1e-15)
+    assert ref.silu(0.0) == 0.0 and abs(ref.silu(40.0) - 40.0) < 1e-12 and abs(ref.silu(-40.0)) < 1e-15
+
+
+def _stack(rng, d, h, nb):
+    return [(rng.standard_normal((h, d)) * 0.05, rng.standard_normal((h, d)) * 0.05, rng.standard_normal((d, h)) * 0.05)
+            for _ in range(nb)]
+
+
+def test_stack_calibrates_each_layer_on_quantized_outputs():
+    rng = np.random.default_rng(12)
+    d, h, n = 16, 24, 300
+    X0 = ref.round16(rng.standard_normal((n, d)), "bfloat16")
+    blocks = _stack(rng, d, h, 2)
+    recs, Xout = ref.quantize_mlp_stack(X0, blocks, bits=3)
+    r0, r1 = recs
+    # down's calibration input is silu(gate) * up of the QUANTIZED gate and up
+    G = ref.round16(X0 @ ref.round16(r0["gate"]["w_hat"], "bfloat16").T, "bfloat16")
+    U = ref.round16(X0 @ ref.round16(r0["up"]["w_hat"], "bfloat16").T, "bfloat16")
+    np.testing.assert_array_equal(r0["Z"], ref.round16(ref.silu(G) * U, "bfloat16"))
+    # ... and differs from what the float weights would give
+    Gf = ref.round16(X0 @ ref.round16(blocks[0][0], "bfloat16").T, "bfloat16")
+    assert np.abs(Gf - G).max() > 1e-3
+    # block 2 reads block 1's quantized output; the next H is that input's
+    np.testing.assert_array_equal(r1["X"], ref.round16(r0["Z"] @ ref.round16(r0["down"]["w_hat"], "bfloat16").T,
+                                                       "bfloat16"))
+    np.testing.assert_allclose(r1["H"], ref.hessian(r1["X"]), rtol=1e-12)
+    # gate and up share the block's Hessian: each equals a stand-alone GPTQ on it
+    np.testing.assert_array_equal(r0["up"]["codes"], ref.gptq_quantize(blocks[0][1], r0["H"], 3)["codes"])
+    assert Xout.shape == (n, d)
+
+
+def test_stack_with_fine_grid_tracks_the_float_stack():
+    rng = np.random.default_rng(13)
+    d, h, n = 16, 32, 400
+    X0 = ref.round16(rng.standard_normal((n, d)), "bfloat16")
+    blocks = _stack(rng, d, h, 2)
+    _, Xq = ref.quantize_mlp_stack(X0, blocks, bits=8)
+    X = X0
+    for Wg, Wu, Wd in blocks:
+        Z = ref.silu(X @ Wg.T) * (X @ Wu.T)
+        X = Z @ Wd.T
+    assert np.linalg.norm(Xq - X) / np.linalg.norm(X) < 0.02
+    _, X3 = ref.quantize_mlp_stack(X0, blocks, bits=3)
+    assert np.linalg.norm(X3 - X) > np.linalg.norm(Xq - X)          # coarser grid, larger drift
+
