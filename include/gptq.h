@@ -250,6 +250,35 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
                                  int64_t lda, int64_t block, void* out, gptq_dtype ot,
                                  int64_t ldo, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Forward pass of a quantized linear layer over calibration tokens, for the
+ * layer-by-layer pass.  Page: "What is GPTQ" (queryfeedz glossary), section
+ * "How it works": each layer is quantized in turn and the next layer is
+ * calibrated on the quantized outputs of the previous one.
+ *
+ *   act == 0:  Y[t, i] = round_yt( sum_k X[t, k] * round_xt(W_hat[i, k]) )
+ *   act == 1:  Y[t, i] = round_yt( silu(G[t, i]) * round_xt(sum_k ...) ),
+ *              silu(g) = g / (1 + exp(-g)): the gated MLP's silu(gate) * up.
+ *
+ * W_hat is the dequantized weight matrix gptq_quantize_layer writes (fp32,
+ * original column order); it is rounded once (round-to-nearest-even) to the
+ * activations' 16-bit type, the model's own precision.  Products are exact in
+ * fp32, sums are fp32 (matrix cores), results are rounded once to yt.
+ *
+ * X     : n_tok x d, xt = GPTQ_BF16 or GPTQ_F16, row stride ldx (multiple of
+ *         8), 16-byte aligned.
+ * W_hat : r x d fp32, row stride ldw (multiple of 4), 16-byte aligned.
+ * G     : n_tok x r of type xt, row stride ldg (act == 1 only; may be NULL
+ *         otherwise).
+ * Y     : n_tok x r of type yt, row stride ldy.  Y may be G itself (same type
+ *         and stride); any other overlap with X, W_hat or G is GPTQ_EINVAL.
+ * Requires d a positive multiple of 64.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int64_t d,
+                                int64_t ldx, const float* W_hat, int64_t r, int64_t ldw,
+                                int act, const void* G, int64_t ldg, void* Y, gptq_dtype yt,
+                                int64_t ldy, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* gptq_status_string(gptq_status s);
 /* Detail of the last failure on the calling thread (thread-local storage). */

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libgptq_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["gptq_api.hip", "gemm_f32.hip", "syrk.hip", "prepare.hip", "quantize.hip", "pack.hip", "gemv.hip", "hadamard.hip"]
+SOURCES = ["gptq_api.hip", "gemm_f32.hip", "syrk.hip", "prepare.hip", "quantize.hip", "pack.hip", "gemv.hip", "hadamard.hip", "linear.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -261,4 +261,40 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
   return check_launch(fn);
 }
 
+// ------------------------------------------------------------------ quantized linear forward
+gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int64_t d, int64_t ldx,
+                                const float* W_hat, int64_t r, int64_t ldw, int act, const void* G, int64_t ldg,
+                                void* Y, gptq_dtype yt, int64_t ldy, void* stream) {
+  const char* fn = "gptq_linear_forward";
+  if (n_tok < 0 || d < 0 || r < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (!valid_dtype(xt) || !valid_dtype(yt)) return fail(GPTQ_EINVAL, fn, "xt and yt must be gptq_dtype values");
+  if (xt == GPTQ_F32) return fail(GPTQ_EDTYPE, fn, "X must be GPTQ_BF16 or GPTQ_F16");
+  if (act != 0 && act != 1) return fail(GPTQ_EINVAL, fn, "act must be 0 (none) or 1 (silu(G) * up)");
+  if (d < 64 || d % 64 != 0) return fail(GPTQ_EUNSUPPORTED, fn, "d must be a positive multiple of 64");
+  if (r > (int64_t)INT_MAX / 2 || d > (int64_t)INT_MAX / 2 || n_tok > kMaxRows)
+    return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (n_tok == 0 || r == 0) return ok();
+  if (ldx < d || ldw < d || ldy < r || (act == 1 && ldg < r)) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");
+  if (!X || !W_hat || !Y || (act == 1 && !G)) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
+  if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(W_hat, 16) || ldw % 4 != 0)
+    return fail(GPTQ_EALIGN, fn, "X and W_hat rows must start on 16 bytes");
+  if (!aligned(Y, elem_size(yt)) || (act == 1 && !aligned(G, 2))) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
+  const char* y0 = static_cast<const char*>(Y);
+  const char* y1 = y0 + ((n_tok - 1) * ldy + r) * (int64_t)elem_size(yt);
+  const char* x0 = static_cast<const char*>(X);
+  const char* x1 = x0 + ((n_tok - 1) * ldx + d) * 2;
+  const char* w0 = reinterpret_cast<const char*>(W_hat);
+  const char* w1 = w0 + ((r - 1) * ldw + d) * 4;
+  if ((y0 < x1 && x0 < y1) || (y0 < w1 && w0 < y1)) return fail(GPTQ_EINVAL, fn, "Y overlaps X or W_hat");
+  if (act == 1) {
+    const char* g0 = static_cast<const char*>(G);
+    const char* g1 = g0 + ((n_tok - 1) * ldg + r) * 2;
+    if (y0 < g1 && g0 < y1 && !(Y == G && yt == xt && ldy == ldg))
+      return fail(GPTQ_EINVAL, fn, "Y overlaps G (only Y == G with the same type and stride is allowed)");
+  }
+  gptq::launch_linear(X, (int)xt, n_tok, d, ldx, W_hat, r, ldw, act, G, ldg, Y, (int)yt, ldy,
+                      reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
 }  // extern "C"

@@ -77,6 +77,11 @@ void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, const int
 void launch_hadamard(const void* A, int at, int64_t lda, int64_t rows, int64_t d, int64_t block, void* out,
                      int ot, int64_t ldo, hipStream_t s);
 
+// --- Quantized linear forward over the calibration tokens (linear.hip) ---
+// xt: 1 bf16, 2 f16; yt: 0 f32, 1 bf16, 2 f16; act: 0 none, 1 silu(G) * up.
+void launch_linear(const void* X, int xt, int64_t n_tok, int64_t d, int64_t ldx, const float* W, int64_t r,
+                   int64_t ldw, int act, const void* G, int64_t ldg, void* Y, int yt, int64_t ldy, hipStream_t s);
+
 // --- Dequantize-on-the-fly product (gemv.hip) ---
 struct GemvPlan {
   int S;         // waves sharing one row's columns (0: c too large)

@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import GPTQ_BF16, GPTQ_F16, GPTQ_F32, GPTQError
 
-__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "hadamard_rotate", "Workspace",
+__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "hadamard_rotate",
+           "linear_forward", "Workspace",
            "NotPositiveDefinite", "GPTQError"]
 
 _DT = {torch.float32: GPTQ_F32, torch.bfloat16: GPTQ_BF16, torch.float16: GPTQ_F16}
@@ -226,6 +227,34 @@ def hadamard_rotate(A: torch.Tensor, block: int = 0, out: torch.Tensor | None = 
         raise ValueError("out must match A's shape with contiguous rows")
     m, d = A.shape
     _lib.call("gptq_hadamard_rotate", _ptr(A), _DT[A.dtype], m, d, A.stride(0), int(block), _ptr(out),
+              _DT[out.dtype], out.stride(0), _stream())
+    return out
+
+
+def linear_forward(X: torch.Tensor, W_hat: torch.Tensor, gate: torch.Tensor | None = None,
+                   out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """Y = X W_hat^T over calibration tokens (W_hat rounded to X's 16-bit type,
+    fp32 sums), or silu(gate) * round(X W_hat^T) when gate is given."""
+    _need(X, "X", None, 2)
+    dev = X.device
+    _need(W_hat, "W_hat", torch.float32, 2, dev)
+    if X.dtype not in (torch.bfloat16, torch.float16) or X.stride(1) != 1 or W_hat.stride(1) != 1:
+        raise ValueError("X must be bf16/fp16 and X, W_hat must have contiguous rows")
+    n, d = X.shape
+    r = W_hat.shape[0]
+    if W_hat.shape[1] != d:
+        raise ValueError("W_hat must be r x d")
+    if gate is not None:
+        _need(gate, "gate", X.dtype, 2, dev)
+        if gate.shape != (n, r) or gate.stride(1) != 1:
+            raise ValueError("gate must be n_tok x r with contiguous rows")
+    if out is None:
+        out = torch.empty((n, r), dtype=out_dtype or X.dtype, device=dev)
+    _need(out, "out", None, 2, dev)
+    if out.shape != (n, r) or out.dtype not in _DT or out.stride(1) != 1:
+        raise ValueError("out must be n_tok x r with contiguous rows")
+    _lib.call("gptq_linear_forward", _ptr(X), _DT[X.dtype], n, d, X.stride(0), _ptr(W_hat), r, W_hat.stride(0),
+              1 if gate is not None else 0, _ptr(gate), gate.stride(0) if gate is not None else 0, _ptr(out),
               _DT[out.dtype], out.stride(0), _stream())
     return out
 

