@@ -18,7 +18,8 @@
 // 64, with each 16-byte run of 8 K-values written to an LDS row of 128 bytes
 // whose chunks are XOR-swizzled by the row (conflict-free MFMA operand reads).
 // W_hat is read as fp32 and rounded on its way into LDS.  Two LDS buffers:
-// the loads of step s+2 are in flight while step s computes.  Consecutive
+// the loads of step s+2 are in flight while step s computes, and the first
+// MFMA operands of a step are read before the next step is staged.  Consecutive
 // workgroups share the same X rows (the larger operand), which the caches
 // then serve to all the column tiles.
 #include "common.hpp"
@@ -82,10 +83,9 @@ struct LinArgs {
 };
 
 template <int DT, int ACT, int YT>
-GPTQ_DEV void store_out(const LinArgs& a, int64_t gm, int gn, float y) {
+GPTQ_DEV void store_out(const LinArgs& a, int64_t gm, int gn, float y, float g) {
   if constexpr (ACT == 1) {
     const float u = from16<DT>((uint16_t)to16<DT>(y));
-    const float g = from16<DT>(a.G[gm * a.ldg + gn]);
     // silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (a few
     // ulp of fp32, far below the 16-bit rounding that follows)
     y = __fdividef(g, 1.0f + __expf(-g)) * u;
@@ -158,31 +158,44 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(LinArgs a) {
   stage(0);
   if (nsteps > 1) fetch(1);
   __syncthreads();
+  u32x4 fa[2][4], fb[2][4];
+  auto frags = [&](const unsigned char* as, const unsigned char* bs, int kk, u32x4 (&xa)[4], u32x4 (&xb)[4]) {
+    const int chunk = 2 * kk + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int f = wm + 32 * i + (lane & 31);
+      xa[i] = *reinterpret_cast<const u32x4*>(as + f * LROWB + ((chunk ^ lswz(f)) * 16));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int f = wn + 32 * j + (lane & 31);
+      xb[j] = *reinterpret_cast<const u32x4*>(bs + f * LROWB + ((chunk ^ lswz(f)) * 16));
+    }
+  };
+  auto mfmas = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = lmfma<DT>(xa[i], xb[j], acc[i][j]);
+  };
+  // Step st computes from LDS buffer st & 1.  The first two sub-steps'
+  // operands are read before the next step's words are written to the other
+  // buffer and the loads of step st+2 issued, so the MFMAs start at once;
+  // the later operands are read while earlier MFMAs run.
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
-    if (st + 1 < nsteps) stage(buf ^ 1);
-    if (st + 2 < nsteps) fetch(st + 2);
     const unsigned char* as = a_buf(buf);
     const unsigned char* bs = b_buf(buf);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int chunk = 2 * kk + (lane >> 5);
-      u32x4 fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int f = wm + 32 * i + (lane & 31);
-        fa[i] = *reinterpret_cast<const u32x4*>(as + f * LROWB + ((chunk ^ lswz(f)) * 16));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = wn + 32 * j + (lane & 31);
-        fb[j] = *reinterpret_cast<const u32x4*>(bs + f * LROWB + ((chunk ^ lswz(f)) * 16));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = lmfma<DT>(fa[i], fb[j], acc[i][j]);
-    }
+    frags(as, bs, 0, fa[0], fb[0]);
+    frags(as, bs, 1, fa[1], fb[1]);
+    if (st + 1 < nsteps) stage(buf ^ 1);
+    if (st + 2 < nsteps) fetch(st + 2);
+    mfmas(fa[0], fb[0]);
+    frags(as, bs, 2, fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+    frags(as, bs, 3, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
     __syncthreads();
   }
 
@@ -201,11 +214,25 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(LinArgs a) {
       for (int v = 0; v < 16; ++v)
         ep[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * 128 + 32 * j + (lane & 31)] = acc[i][j][v];
     __syncthreads();
-    for (int e = 0; e < 64; ++e) {
-      const int idx = e * 64 + lane, row = idx >> 7, col = idx & 127;
-      const int64_t gm = m0 + wm + 32 * i + row;
-      const int gn = n0 + wn + col;
-      if (gm < a.M && gn < a.N) store_out<DT, ACT, YT>(a, gm, gn, ep[idx]);
+    // 32 outputs per lane at a time; their gate values are all requested
+    // before any is used
+#pragma unroll 1
+    for (int c = 0; c < 2; ++c) {
+      float gv[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int idx = (32 * c + e) * 64 + lane, row = idx >> 7, col = idx & 127;
+        const int64_t gm = m0 + wm + 32 * i + row;
+        const int gn = n0 + wn + col;
+        gv[e] = (ACT == 1 && gm < a.M && gn < a.N) ? from16<DT>(a.G[gm * a.ldg + gn]) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const int idx = (32 * c + e) * 64 + lane, row = idx >> 7, col = idx & 127;
+        const int64_t gm = m0 + wm + 32 * i + row;
+        const int gn = n0 + wn + col;
+        if (gm < a.M && gn < a.N) store_out<DT, ACT, YT>(a, gm, gn, ep[idx], gv[e]);
+      }
     }
   }
 }
