@@ -9,13 +9,22 @@
 // Work split: 256 x 256 output tiles of the upper triangle, times `splits`
 // contiguous token ranges.  Each workgroup (4 waves, each a 128 x 128 block of
 // the tile as 4 x 4 MFMA blocks, accumulators in AGPRs) streams its token range
-// in K-steps of 64.  A K-step of X arrives feature-contiguous; each thread loads
-// an 8-token x 8-feature patch of each slab (eight 16-byte buffer loads),
-// transposes it in registers with v_perm_b32, and writes eight 16-byte
-// token-contiguous rows into LDS, so every MFMA operand is a single 16-byte LDS
-// read.  The loads run two K-steps ahead.  LDS rows are 128 bytes (64 tokens)
-// with the 16-byte chunks XOR-swizzled by the row index, which keeps both the
-// transposed writes and the MFMA reads free of bank conflicts.
+// in K-steps of 64.  X arrives feature-contiguous (token rows), while an MFMA
+// operand wants 8 consecutive tokens of one feature.  Two data paths:
+//  * interior tiles (both 256-feature slabs inside [0, d), X 16-byte aligned,
+//    ldx % 8 == 0, ldx < 2^24): buffer loads that write LDS directly carry each
+//    K-step's token rows of both slabs into LDS one step ahead of the MFMAs
+//    (no registers, no transposes in the ALU); the operands are read back with
+//    the LDS transpose read ds_read_b64_tr_b16, which hands each lane four
+//    consecutive tokens of one feature.  LDS rows are 512 bytes (one token, 256
+//    features) with 16-byte chunk c stored at chunk position c ^ ((row & 3) << 2),
+//    so the 16 lanes of a transpose read hit distinct banks;
+//  * edge tiles and unaligned X: each thread loads an 8-token x 8-feature patch
+//    of each slab through a bounds-checked loader, transposes it in registers
+//    with v_perm_b32, and writes eight 16-byte token-contiguous rows into LDS
+//    (128-byte rows, chunks XOR-swizzled by the row index), two K-steps ahead.
+// Both paths read the same products and add them in the same order, so the
+// result does not depend on which one a tile takes.
 // With one split the tile is added straight into H; otherwise each workgroup
 // writes its partial tile to the workspace and a second kernel sums the
 // partials of every tile in split order (deterministic, no floating-point
@@ -32,6 +41,10 @@ namespace {
 constexpr int TILE = 256;
 constexpr int KSTEP = 64;
 constexpr int ROWB = KSTEP * 2;  // bytes per LDS row (64 x 16-bit)
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 GPTQ_DEV int swz(int f) { return (f ^ (f >> 3)) & 7; }
 
@@ -104,12 +117,8 @@ GPTQ_DEV floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c) {
   }
 }
 
-// The K-loop of one tile over tokens [t_beg, t_end).  FAST: the tile's
-// feature slabs lie inside [0, d) and X is 16-byte aligned with ldx % 8 == 0,
-// so every patch row is one buffer load; rows past t_end fall outside the
-// descriptor's records and load zeros.  Otherwise the patches go through the
-// bounds-checked loader.  The two variants are separate loops, so no
-// register copies sit between the issue of a load and its use.
+// The K-loop of one tile over tokens [t_beg, t_end) through the
+// bounds-checked loader (edge tiles, unaligned X).
 //
 // Software pipeline over K-steps of 64 tokens: at the start of step s the
 // registers hold the raw patches of step s+1.  They are transposed into the
@@ -117,7 +126,7 @@ GPTQ_DEV floatx16 mfma16(u32x4 a, u32x4 b, floatx16 c) {
 // issued into the freed registers, before step s's MFMAs (LDS buffer s&1).
 // MFMA operands of the next 16-token sub-step are read from LDS while the
 // current sub-step's MFMAs run.
-template <int DT, bool VEC, bool FAST, bool DIAG>
+template <int DT, bool VEC, bool DIAG>
 GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_beg, int64_t t_end, int d,
                          int fi0, int fj0, bool compute_lower, int wm, int wn, unsigned char* smem,
                          floatx16 (&acc)[4][4]) {
@@ -131,29 +140,11 @@ GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_
   const int tb = tid >> 5, fb = tid & 31;
   u32x4 ra0[8], rb0[8];
   const int64_t nsteps = (t_end - t_beg + KSTEP - 1) / KSTEP;
-  // byte offset of the thread's patch inside a token row
-  const int off_a = 2 * (fi0 + fb * 8), off_b = 2 * (fj0 + fb * 8);
 
   auto fetch = [&](int64_t st, u32x4 (&ra)[8], u32x4 (&rb)[8]) {
     const int64_t t0 = t_beg + st * KSTEP + tb * 8;
-    if constexpr (FAST) {
-      // One descriptor per K-step (wave-uniform): base at the step's first
-      // token row, records up to t_end, so rows past t_end load zeros.  The
-      // thread's row and feature offset go in the VGPR offset.
-      const int64_t ts = t_beg + st * KSTEP;
-      const int64_t nrec = min((t_end - ts) * ldx * 2, (int64_t)0x7fffffff);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(X + ts * ldx), (short)0, (int)nrec, 0x00020000);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ro = (tb * 8 + i) * (int)ldx * 2;
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ro + off_a, 0, 0));
-        if (!diag) rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ro + off_b, 0, 0));
-      }
-    } else {
-      load_patch<VEC>(X, ldx, t0, t_end, fi0 + fb * 8, d, ra);
-      if (!diag) load_patch<VEC>(X, ldx, t0, t_end, fj0 + fb * 8, d, rb);
-    }
+    load_patch<VEC>(X, ldx, t0, t_end, fi0 + fb * 8, d, ra);
+    if (!diag) load_patch<VEC>(X, ldx, t0, t_end, fj0 + fb * 8, d, rb);
   };
   // Transpose feature rows m0 .. m0+3 of a patch and write them to LDS.
   auto stage4 = [&](unsigned char* lds, const u32x4 (&rg)[8], int m0) {
@@ -217,35 +208,113 @@ GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_
     }
     __syncthreads();
   };
-  // The same step without branches (st + 2 < nsteps, every wave computes), so
-  // that the transposes, LDS writes and loads share one scheduling region with
-  // the MFMAs.
-  auto steady = [&](int64_t st, int buf, u32x4 (&na)[8], u32x4 (&nb)[8]) {
-    const unsigned char* as = a_buf(buf);
-    const unsigned char* bs = diag ? a_buf(buf) : b_buf(buf);
-    frags(as, bs, 0, fa[0], fbm[0]);
-    frags(as, bs, 1, fa[1], fbm[1]);
-    stage(buf ^ 1, na, nb);
-    fetch(st + 2, na, nb);
-    mfmas(fa[0], fbm[0]);
-    frags(as, bs, 2, fa[0], fbm[0]);
-    mfmas(fa[1], fbm[1]);
-    frags(as, bs, 3, fa[1], fbm[1]);
-    mfmas(fa[0], fbm[0]);
-    mfmas(fa[1], fbm[1]);
-    __syncthreads();
-  };
-
   if (nsteps > 0) {
     fetch(0, ra0, rb0);
     stage(0, ra0, rb0);
     if (nsteps > 1) fetch(1, ra0, rb0);
     __syncthreads();
-    int64_t st = 0;
-    if constexpr (FAST && !DIAG) {
-      for (; st + 2 < nsteps; ++st) steady(st, (int)(st & 1), ra0, rb0);
+    for (int64_t st = 0; st < nsteps; ++st) step(st, (int)(st & 1), ra0, rb0);
+  }
+}
+
+// The K-loop of one interior tile (see the header): K-step st's token rows
+// of both slabs are carried into LDS buffer st & 1 by buffer loads that write
+// LDS, issued before step st-1's MFMAs; one wait and one barrier per step.
+// LDS buffer b holds slab A at b * 64 KiB and slab B 32 KiB after it, each 64
+// token rows of 512 bytes.
+GPTQ_DEV int dsw(int r) { return (r & 3) << 2; }
+
+template <int DT, bool DIAG>
+GPTQ_DEV void syrk_steps_dma(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_beg, int64_t t_end,
+                             int fi0, int fj0, bool compute, int wm, int wn, unsigned char* smem,
+                             floatx16 (&acc)[4][4]) {
+  constexpr int SLAB = KSTEP * 512, BUF = 2 * SLAB;
+  // Each load instruction of a wave moves two token rows of one slab (32
+  // lanes x 16 bytes each); a wave issues 8 per slab and step.
+  constexpr int NI = KSTEP / 2 / 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  lds_u8* lbase = (lds_u8*)smem;  // generic to LDS address space
+  const int64_t nsteps = (t_end - t_beg + KSTEP - 1) / KSTEP;
+  auto dma = [&](int64_t st, int b) {
+    // One descriptor per K-step (wave-uniform): base at the step's first
+    // token row, records up to t_end, so rows past t_end load zeros.  With
+    // ldx < 2^24 every offset of the step fits the 32-bit VGPR offset.
+    const int64_t ts = t_beg + st * KSTEP;
+    const int64_t nrec = min((t_end - ts) * ldx * 2, (int64_t)0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(X + ts * ldx), (short)0, (int)nrec, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int I = wave * NI + q;
+      const int r = 2 * I + (lane >> 5), c = (lane & 31) ^ dsw(r);
+      const int ro = r * (int)ldx * 2;
+      // lane l of the instruction lands at LDS base + 16 l: row r, position
+      // lane & 31, which holds chunk c of the row.
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lbase + b * BUF + I * 1024, 16, ro + (fi0 + 8 * c) * 2, 0, 0, 0);
+      if (!DIAG)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lbase + b * BUF + SLAB + I * 1024, 16,
+                                                 ro + (fj0 + 8 * c) * 2, 0, 0, 0);
     }
-    for (; st < nsteps; ++st) step(st, (int)(st & 1), ra0, rb0);
+  };
+  // Four 16-bit values of token row r at slab features fo .. fo+3 (fo % 4 == 0)
+  // as read by one lane of a transpose read: the 16 lanes of a group that read
+  // rows r0 + (i >> 2), features fo0 + 4 (i & 3), receive, lane i, the values
+  // of feature fo0 + i % 16 ... at the four rows r0 .. r0+3.
+  auto tr = [&](const lds_u8* slab, int r, int fo) {
+    const int off = r * 512 + ((((fo >> 3) ^ dsw(r))) << 4) + ((fo & 7) >> 2) * 8;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(slab + off));
+  };
+  // The 32x32x16 MFMA operand of lane (G = lane >> 4, j = lane & 15) is feature
+  // base_f + 16 (G & 1) + j at tokens 16 kk + 8 (G >> 1) .. +7: two transpose
+  // reads of four tokens each.
+  const int G = lane >> 4, j = lane & 15;
+  auto frag = [&](const lds_u8* slab, int base_f, int kk) {
+    const int row0 = 16 * kk + 8 * (G >> 1) + (j >> 2);
+    const int fo = base_f + 16 * (G & 1) + 4 * (j & 3);
+    const v4s lo = tr(slab, row0, fo), hi = tr(slab, row0 + 4, fo);
+    u32x4 v;
+    v[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+    v[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+    v[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+    v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+    return v;
+  };
+  u32x4 fa[2][4], fb[2][4];
+  auto frags = [&](int b, int kk, u32x4 (&a)[4], u32x4 (&bb)[4]) {
+    const lds_u8* sa = lbase + b * BUF;
+    const lds_u8* sb = DIAG ? sa : sa + SLAB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = frag(sa, wm + 32 * i, kk);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) bb[jj] = frag(sb, wn + 32 * jj, kk);
+  };
+  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&bb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma16<DT>(a[i], bb[jj], acc[i][jj]);
+  };
+  if (nsteps <= 0) return;
+  dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t st = 0; st < nsteps; ++st) {
+    const int b = (int)(st & 1);
+    if (st + 1 < nsteps) dma(st + 1, b ^ 1);
+    if (compute) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEP / 16; kk += 2) {
+        frags(b, kk, fa[0], fb[0]);
+        frags(b, kk + 1, fa[1], fb[1]);
+        mfmas(fa[0], fb[0]);
+        mfmas(fa[1], fb[1]);
+      }
+    }
+    // step st+1 has landed (own loads), in every wave (barrier); buffer b is
+    // free for step st+2.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 }
 
@@ -281,14 +350,15 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // VEC: X 16-byte aligned, ldx % 8 == 0 and ldx < 2^24 (checked by the launcher).
   const bool fast = VEC && fi0 + TILE <= d && fj0 + TILE <= d;
-#define GPTQ_STEPS(F, D) syrk_steps<DT, VEC, F, D>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc)
   if (fast) {
-    if (diag) GPTQ_STEPS(true, true); else GPTQ_STEPS(true, false);
+    if (diag) syrk_steps_dma<DT, true>(X, ldx, t_beg, t_end, fi0, fj0, compute, wm, wn, smem, acc);
+    else syrk_steps_dma<DT, false>(X, ldx, t_beg, t_end, fi0, fj0, compute, wm, wn, smem, acc);
   } else {
-    if (diag) GPTQ_STEPS(false, true); else GPTQ_STEPS(false, false);
+    if (diag) syrk_steps<DT, VEC, true>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc);
+    else syrk_steps<DT, VEC, false>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc);
   }
-#undef GPTQ_STEPS
 
   // Epilogue.  Lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] per block.
   if (part == nullptr) {
@@ -405,7 +475,7 @@ void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok,
   }
   dim3 grid((unsigned)(p.tiles * p.splits));
   float* part = p.splits > 1 ? ws : nullptr;
-  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
+  const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0) && ldx < (int64_t(1) << 24);
   const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
 #define GPTQ_SYRK_LAUNCH(DT, V)                                                                        \
   hipLaunchKernelGGL((syrk16_kernel<DT, V>), grid, dim3(256), shmem, s, Xh, ldx, n_tok, (int)d, nt, \

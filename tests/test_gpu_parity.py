@@ -137,6 +137,40 @@ def test_hessian_matches_oracle(xdtype, n, d, batches, pad):
     check_h(H, ref.hessian(X))
 
 
+@pytest.mark.parametrize("ldx", [(1 << 24) - 64, (1 << 24) + 64])
+def test_hessian_huge_row_stride(ldx):
+    """Row strides at the limit of the interior-tile path (64 token rows of one
+    K-step must stay within 2^31 bytes of the step's first row) and just past
+    it, where every tile takes the bounds-checked loader."""
+    n, d = 100, 512
+    print(f"\n[hessian] n={n} d={d} ldx={ldx}", flush=True)
+    X = S.activations_host(n, d, "t4", outliers=4, gain=20.0, wid=57, dtype="bfloat16")
+    big = torch.zeros((n, ldx), dtype=torch.bfloat16, device="cuda")
+    big[:, :d] = to_dev(X, torch.bfloat16)
+    H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    gq().hessian_accumulate(H, big[:, :d])
+    torch.cuda.synchronize()
+    del big
+    torch.cuda.empty_cache()
+    check_h(H, ref.hessian(X))
+
+
+def test_hessian_data_paths_agree_bitwise():
+    """Interior tiles of aligned X go through the LDS-direct loads, unaligned X
+    through the register-transpose loader; both feed the same products to the
+    MFMAs in the same order, so the Hessians are bitwise equal."""
+    n, d = 3000, 768
+    X = to_dev(S.activations_host(n, d, "t4", outliers=4, gain=20.0, wid=58, dtype="bfloat16"), torch.bfloat16)
+    shifted = torch.zeros((n, d + 8), dtype=torch.bfloat16, device="cuda")
+    shifted[:, 1:1 + d] = X                 # rows start 2 bytes past a 16-byte boundary
+    Ha = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    Hb = torch.zeros_like(Ha)
+    gq().hessian_accumulate(Ha, X)
+    gq().hessian_accumulate(Hb, shifted[:, 1:1 + d])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.triu(Ha), torch.triu(Hb))
+
+
 # -------------------------------------------------------------------- prepare
 @pytest.mark.parametrize("d,act_order,n_dead", [(128, False, 0), (256, True, 2), (300, False, 1),
                                                 (513, True, 3), (1000, False, 0)])
