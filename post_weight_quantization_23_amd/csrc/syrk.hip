@@ -28,9 +28,13 @@
 // With one split the tile is added straight into H; otherwise each workgroup
 // writes its partial tile to the workspace and a second kernel sums the
 // partials of every tile in split order (deterministic, no floating-point
-// atomics) and adds twice the sum into H.  Consecutive workgroups take
-// consecutive tiles of the same token range, so the eight XCDs stream the same
-// rows of X at the same time and share them in the memory-side cache.
+// atomics) and adds twice the sum into H.  Work items (split, tile) are
+// numbered split-major with the tiles of a split in super-tile order; the
+// dispatcher deals workgroups round-robin to the eight XCDs, so within every
+// 256 workgroups XCD x is handed the 32 consecutive work items 32x .. 32x+31:
+// the tiles resident on one XCD share row and column slabs in its L2, and all
+// XCDs work on the same one or two token ranges, which stay in the memory-side
+// cache.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -327,7 +331,11 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
   // LDS: A buffers 0/1 then B buffers 0/1, TILE rows of ROWB bytes each.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  const int split = (int)blockIdx.x / tiles, tile = (int)blockIdx.x % tiles;
+  // Workgroup b runs on XCD b % 8; within each full run of 256 workgroups it
+  // takes work item 32 (b % 8) + (b % 256) / 8 of that run (a bijection).
+  int w = (int)blockIdx.x;
+  if (w < ((tiles * splits) & ~255)) w = (w & ~255) | ((w & 7) << 5) | ((w & 255) >> 3);
+  const int split = w / tiles, tile = w % tiles;
   int bi, bj;
   tile_coords(tile, nt, bi, bj);
   const bool diag = bi == bj;
