@@ -261,13 +261,17 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
  *              silu(g) = g / (1 + exp(-g)): the gated MLP's silu(gate) * up.
  *
  * W_hat is the dequantized weight matrix gptq_quantize_layer writes (fp32,
- * original column order); it is rounded once (round-to-nearest-even) to the
- * activations' 16-bit type, the model's own precision.  Products are exact in
- * fp32, sums are fp32 (matrix cores), results are rounded once to yt.
+ * original column order), rounded once (round-to-nearest-even) to the
+ * activations' 16-bit type, the model's own precision: either inside this
+ * call (wt = GPTQ_F32) or beforehand by gptq_round16 (wt = xt); the results
+ * are the same bit for bit.  Products are exact in fp32, sums are fp32
+ * (matrix cores), results are rounded once to yt.
  *
  * X     : n_tok x d, xt = GPTQ_BF16 or GPTQ_F16, row stride ldx (multiple of
  *         8), 16-byte aligned.
- * W_hat : r x d fp32, row stride ldw (multiple of 4), 16-byte aligned.
+ * W_hat : r x d of type wt (GPTQ_F32, or xt), row stride ldw (a multiple of
+ *         4 for fp32, of 8 for 16-bit), 16-byte aligned.  With 16-bit
+ *         W_hat, ldx and ldw must be below 2^22 (GPTQ_EUNSUPPORTED).
  * G     : n_tok x r of type xt, row stride ldg (act == 1 only; may be NULL
  *         otherwise).
  * Y     : n_tok x r of type yt, row stride ldy.  Y may be G itself (same type
@@ -275,9 +279,26 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
  * Requires d a positive multiple of 64.
  * ------------------------------------------------------------------------ */
 gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int64_t d,
-                                int64_t ldx, const float* W_hat, int64_t r, int64_t ldw,
-                                int act, const void* G, int64_t ldg, void* Y, gptq_dtype yt,
-                                int64_t ldy, void* stream);
+                                int64_t ldx, const void* W_hat, gptq_dtype wt, int64_t r,
+                                int64_t ldw, int act, const void* G, int64_t ldg, void* Y,
+                                gptq_dtype yt, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Rounds fp32 values to a 16-bit type, element by element:
+ *   dst[i, j] = round_dt(src[i, j]),  round-to-nearest-even; bf16 keeps NaN
+ *   (quiet), fp16 overflows to infinity.
+ * The rounding of the dequantized weights that the layer-by-layer forward
+ * applies (same page and section as gptq_linear_forward), as a pass of its
+ * own so that a layer's weights are rounded once rather than once per token
+ * tile.
+ *
+ * src : rows x cols fp32, row stride lds, 4-byte aligned.
+ * dst : rows x cols of type dt (GPTQ_BF16 or GPTQ_F16), row stride ldd,
+ *       2-byte aligned; must not overlap src (GPTQ_EINVAL).
+ * Stream-ordered and asynchronous; the caller owns both buffers.
+ * ------------------------------------------------------------------------ */
+gptq_status gptq_round16(const float* src, int64_t rows, int64_t cols, int64_t lds,
+                         gptq_dtype dt, void* dst, int64_t ldd, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* gptq_status_string(gptq_status s);

@@ -4,9 +4,9 @@ matrix-vector product over the packed words, the Hadamard pre-rotation and the
 quantized forward for layer-by-layer calibration, as hand-written HIP kernels
 behind the C ABI in include/gptq.h."""
 from .gptq import (GPTQError, NotPositiveDefinite, Workspace, dequant_gemv, hadamard_rotate, hessian_accumulate,
-                   linear_forward, pack, prepare, quantize_layer)
+                   linear_forward, pack, prepare, quantize_layer, round16)
 from .sequential import quantize_mlp_stack
 
 __all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "hadamard_rotate",
-           "linear_forward", "quantize_mlp_stack", "Workspace",
+           "linear_forward", "round16", "quantize_mlp_stack", "Workspace",
            "NotPositiveDefinite", "GPTQError"]

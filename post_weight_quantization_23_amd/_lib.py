@@ -31,8 +31,9 @@ SIGNATURES = {
     "gptq_pack": (C.c_int, [_P, _I64, _I64, C.c_int, _P, _P, _I64, _P]),
     "gptq_dequant_gemv": (C.c_int, [_P, _I64, _I64, C.c_int, _I64, _P, _P, _I64, _I64, _P, _P, C.c_int, _P, _P]),
     "gptq_hadamard_rotate": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _I64, _P, C.c_int, _I64, _P]),
-    "gptq_linear_forward": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _P, _I64, _I64, C.c_int, _P, _I64, _P,
-                                      C.c_int, _I64, _P]),
+    "gptq_linear_forward": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _P, C.c_int, _I64, _I64, C.c_int, _P, _I64,
+                                      _P, C.c_int, _I64, _P]),
+    "gptq_round16": (C.c_int, [_P, _I64, _I64, _I64, C.c_int, _P, _I64, _P]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_last_error": (C.c_char_p, []),
 }

@@ -263,12 +263,14 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
 
 // ------------------------------------------------------------------ quantized linear forward
 gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int64_t d, int64_t ldx,
-                                const float* W_hat, int64_t r, int64_t ldw, int act, const void* G, int64_t ldg,
-                                void* Y, gptq_dtype yt, int64_t ldy, void* stream) {
+                                const void* W_hat, gptq_dtype wt, int64_t r, int64_t ldw, int act, const void* G,
+                                int64_t ldg, void* Y, gptq_dtype yt, int64_t ldy, void* stream) {
   const char* fn = "gptq_linear_forward";
   if (n_tok < 0 || d < 0 || r < 0) return fail(GPTQ_EINVAL, fn, "negative size");
-  if (!valid_dtype(xt) || !valid_dtype(yt)) return fail(GPTQ_EINVAL, fn, "xt and yt must be gptq_dtype values");
+  if (!valid_dtype(xt) || !valid_dtype(yt) || !valid_dtype(wt))
+    return fail(GPTQ_EINVAL, fn, "xt, wt and yt must be gptq_dtype values");
   if (xt == GPTQ_F32) return fail(GPTQ_EDTYPE, fn, "X must be GPTQ_BF16 or GPTQ_F16");
+  if (wt != GPTQ_F32 && wt != xt) return fail(GPTQ_EDTYPE, fn, "W_hat must be GPTQ_F32 or of X's type");
   if (act != 0 && act != 1) return fail(GPTQ_EINVAL, fn, "act must be 0 (none) or 1 (silu(G) * up)");
   if (d < 64 || d % 64 != 0) return fail(GPTQ_EUNSUPPORTED, fn, "d must be a positive multiple of 64");
   if (r > (int64_t)INT_MAX / 2 || d > (int64_t)INT_MAX / 2 || n_tok > kMaxRows)
@@ -276,15 +278,18 @@ gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int
   if (n_tok == 0 || r == 0) return ok();
   if (ldx < d || ldw < d || ldy < r || (act == 1 && ldg < r)) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");
   if (!X || !W_hat || !Y || (act == 1 && !G)) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
-  if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(W_hat, 16) || ldw % 4 != 0)
+  const bool w16 = wt != GPTQ_F32;
+  if (!aligned(X, 16) || ldx % 8 != 0 || !aligned(W_hat, 16) || ldw % (w16 ? 8 : 4) != 0)
     return fail(GPTQ_EALIGN, fn, "X and W_hat rows must start on 16 bytes");
+  if (w16 && (ldx >= (int64_t(1) << 22) || ldw >= (int64_t(1) << 22)))
+    return fail(GPTQ_EUNSUPPORTED, fn, "16-bit W_hat needs ldx and ldw below 2^22");
   if (!aligned(Y, elem_size(yt)) || (act == 1 && !aligned(G, 2))) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
   const char* y0 = static_cast<const char*>(Y);
   const char* y1 = y0 + ((n_tok - 1) * ldy + r) * (int64_t)elem_size(yt);
   const char* x0 = static_cast<const char*>(X);
   const char* x1 = x0 + ((n_tok - 1) * ldx + d) * 2;
-  const char* w0 = reinterpret_cast<const char*>(W_hat);
-  const char* w1 = w0 + ((r - 1) * ldw + d) * 4;
+  const char* w0 = static_cast<const char*>(W_hat);
+  const char* w1 = w0 + ((r - 1) * ldw + d) * (int64_t)elem_size(wt);
   if ((y0 < x1 && x0 < y1) || (y0 < w1 && w0 < y1)) return fail(GPTQ_EINVAL, fn, "Y overlaps X or W_hat");
   if (act == 1) {
     const char* g0 = static_cast<const char*>(G);
@@ -292,8 +297,29 @@ gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int
     if (y0 < g1 && g0 < y1 && !(Y == G && yt == xt && ldy == ldg))
       return fail(GPTQ_EINVAL, fn, "Y overlaps G (only Y == G with the same type and stride is allowed)");
   }
-  gptq::launch_linear(X, (int)xt, n_tok, d, ldx, W_hat, r, ldw, act, G, ldg, Y, (int)yt, ldy,
+  gptq::launch_linear(X, (int)xt, n_tok, d, ldx, W_hat, w16, r, ldw, act, G, ldg, Y, (int)yt, ldy,
                       reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
+gptq_status gptq_round16(const float* src, int64_t rows, int64_t cols, int64_t lds, gptq_dtype dt, void* dst,
+                         int64_t ldd, void* stream) {
+  const char* fn = "gptq_round16";
+  if (rows < 0 || cols < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (!valid_dtype(dt)) return fail(GPTQ_EINVAL, fn, "dt must be a gptq_dtype value");
+  if (dt == GPTQ_F32) return fail(GPTQ_EDTYPE, fn, "dt must be GPTQ_BF16 or GPTQ_F16");
+  if (rows > kMaxRows || cols > kMaxRows || rows * ((cols + 3) / 4) / 256 >= (int64_t)INT_MAX)
+    return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (rows == 0 || cols == 0) return ok();
+  if (lds < cols || ldd < cols) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");
+  if (!src || !dst) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
+  if (!aligned(src, 4) || !aligned(dst, 2)) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
+  const char* s0 = reinterpret_cast<const char*>(src);
+  const char* s1 = s0 + ((rows - 1) * lds + cols) * 4;
+  const char* d0 = static_cast<const char*>(dst);
+  const char* d1 = d0 + ((rows - 1) * ldd + cols) * 2;
+  if (s0 < d1 && d0 < s1) return fail(GPTQ_EINVAL, fn, "dst overlaps src");
+  gptq::launch_round16(src, rows, cols, lds, (int)dt, dst, ldd, reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);
 }
 

@@ -79,8 +79,13 @@ void launch_hadamard(const void* A, int at, int64_t lda, int64_t rows, int64_t d
 
 // --- Quantized linear forward over the calibration tokens (linear.hip) ---
 // xt: 1 bf16, 2 f16; yt: 0 f32, 1 bf16, 2 f16; act: 0 none, 1 silu(G) * up.
-void launch_linear(const void* X, int xt, int64_t n_tok, int64_t d, int64_t ldx, const float* W, int64_t r,
-                   int64_t ldw, int act, const void* G, int64_t ldg, void* Y, int yt, int64_t ldy, hipStream_t s);
+// W: fp32, or (w16) already rounded to xt's 16-bit type.
+void launch_linear(const void* X, int xt, int64_t n_tok, int64_t d, int64_t ldx, const void* W, bool w16,
+                   int64_t r, int64_t ldw, int act, const void* G, int64_t ldg, void* Y, int yt, int64_t ldy,
+                   hipStream_t s);
+// dst[rows x cols] (16-bit type dt: 1 bf16, 2 f16) = round16(src), element-wise.
+void launch_round16(const float* src, int64_t rows, int64_t cols, int64_t lds, int dt, void* dst, int64_t ldd,
+                    hipStream_t s);
 
 // --- Dequantize-on-the-fly product (gemv.hip) ---
 struct GemvPlan {

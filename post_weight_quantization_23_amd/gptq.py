@@ -234,12 +234,15 @@ def hadamard_rotate(A: torch.Tensor, block: int = 0, out: torch.Tensor | None = 
 def linear_forward(X: torch.Tensor, W_hat: torch.Tensor, gate: torch.Tensor | None = None,
                    out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None) -> torch.Tensor:
     """Y = X W_hat^T over calibration tokens (W_hat rounded to X's 16-bit type,
-    fp32 sums), or silu(gate) * round(X W_hat^T) when gate is given."""
+    fp32 sums), or silu(gate) * round(X W_hat^T) when gate is given.  W_hat is
+    fp32, or already rounded to X's type (round16)."""
     _need(X, "X", None, 2)
     dev = X.device
-    _need(W_hat, "W_hat", torch.float32, 2, dev)
+    _need(W_hat, "W_hat", None, 2, dev)
     if X.dtype not in (torch.bfloat16, torch.float16) or X.stride(1) != 1 or W_hat.stride(1) != 1:
         raise ValueError("X must be bf16/fp16 and X, W_hat must have contiguous rows")
+    if W_hat.dtype not in (torch.float32, X.dtype):
+        raise TypeError("W_hat must be float32 or of X's dtype")
     n, d = X.shape
     r = W_hat.shape[0]
     if W_hat.shape[1] != d:
@@ -253,8 +256,23 @@ def linear_forward(X: torch.Tensor, W_hat: torch.Tensor, gate: torch.Tensor | No
     _need(out, "out", None, 2, dev)
     if out.shape != (n, r) or out.dtype not in _DT or out.stride(1) != 1:
         raise ValueError("out must be n_tok x r with contiguous rows")
-    _lib.call("gptq_linear_forward", _ptr(X), _DT[X.dtype], n, d, X.stride(0), _ptr(W_hat), r, W_hat.stride(0),
-              1 if gate is not None else 0, _ptr(gate), gate.stride(0) if gate is not None else 0, _ptr(out),
-              _DT[out.dtype], out.stride(0), _stream())
+    _lib.call("gptq_linear_forward", _ptr(X), _DT[X.dtype], n, d, X.stride(0), _ptr(W_hat), _DT[W_hat.dtype], r,
+              W_hat.stride(0), 1 if gate is not None else 0, _ptr(gate), gate.stride(0) if gate is not None else 0,
+              _ptr(out), _DT[out.dtype], out.stride(0), _stream())
+    return out
+
+
+def round16(src: torch.Tensor, dtype: torch.dtype, out: torch.Tensor | None = None) -> torch.Tensor:
+    """src (fp32, 2-D, contiguous rows) rounded to bf16 / fp16, round-to-nearest-even."""
+    _need(src, "src", torch.float32, 2)
+    if dtype not in (torch.bfloat16, torch.float16) or src.stride(1) != 1:
+        raise ValueError("dtype must be bf16 or fp16 and src must have contiguous rows")
+    rows, cols = src.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=src.device)
+    _need(out, "out", dtype, 2, src.device)
+    if out.shape != src.shape or out.stride(1) != 1:
+        raise ValueError("out must match src's shape with contiguous rows")
+    _lib.call("gptq_round16", _ptr(src), rows, cols, src.stride(0), _DT[dtype], _ptr(out), out.stride(0), _stream())
     return out
 

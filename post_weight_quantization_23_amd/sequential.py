@@ -11,7 +11,9 @@ down(silu(gate(x)) * up(x)).  For each block: H of the block input (one SYRK,
 shared by gate and up) -> U -> GPTQ of gate and of up -> the quantized gate
 and up forwards (the second fused with silu(gate) * up) -> H of that product
 -> U -> GPTQ of down -> the quantized down forward, which is the next block's
-input.  The forward runs in the activations' 16-bit type (gptq_linear_forward).
+input.  The forward runs in the activations' 16-bit type: each dequantized
+weight matrix is rounded to it once (gptq_round16) and the products read the
+16-bit copy (gptq_linear_forward).
 This module only sequences calls; the arithmetic is in the library.
 """
 from __future__ import annotations
@@ -40,15 +42,17 @@ def quantize_mlp_stack(X0: torch.Tensor, blocks, bits: int = 4, groupsize: int =
         perm, dead, _ = gptq.prepare(U, percdamp, act_order, ws=ws_p)      # H -> U in place
         qg = gptq.quantize_layer(Wg, U, perm, dead, bits, groupsize, blocksize, want_w_hat=True, ws=ws_q)
         qu = gptq.quantize_layer(Wu, U, perm, dead, bits, groupsize, blocksize, want_w_hat=True, ws=ws_q)
-        G = gptq.linear_forward(X, qg["w_hat"])
-        Z = gptq.linear_forward(X, qu["w_hat"], gate=G)
+        w16 = gptq.round16(qg["w_hat"], X.dtype)
+        G = gptq.linear_forward(X, w16)
+        gptq.round16(qu["w_hat"], X.dtype, out=w16)
+        Z = gptq.linear_forward(X, w16, gate=G)
         h = Z.shape[1]
         U2 = torch.zeros((h, h), dtype=torch.float32, device=X.device)
         gptq.hessian_accumulate(U2, Z, ws=ws_h)
         H2 = U2.clone() if keep else None
         perm2, dead2, _ = gptq.prepare(U2, percdamp, act_order, ws=ws_p)
         qd = gptq.quantize_layer(Wd, U2, perm2, dead2, bits, groupsize, blocksize, want_w_hat=True, ws=ws_q)
-        Xn = gptq.linear_forward(Z, qd["w_hat"])
+        Xn = gptq.linear_forward(Z, gptq.round16(qd["w_hat"], Z.dtype))
         rec = {"gate": qg, "up": qu, "down": qd, "U": U, "perm": perm, "U2": U2, "perm2": perm2}
         if keep:
             rec.update({"X": X, "H": H, "G": G, "Z": Z, "H2": H2})

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_symbols_are_exported(lib):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -175,20 +175,40 @@ def test_linear_forward_argument_errors(lib):
     f = "gptq_linear_forward"
     X, W, Y, G = ALIGNED, C.c_void_p(0x1000000), C.c_void_p(0x40000000), C.c_void_p(0x80000000)
 
-    def l(x=X, xt=1, n=8, d=256, ldx=256, w=W, r=64, ldw=256, act=0, g=None, ldg=0, y=Y, yt=1, ldy=64):
-        return _st(lib, f, x, xt, n, d, ldx, w, r, ldw, act, g, ldg, y, yt, ldy, None)
+    def l(x=X, xt=1, n=8, d=256, ldx=256, w=W, wt=0, r=64, ldw=256, act=0, g=None, ldg=0, y=Y, yt=1, ldy=64):
+        return _st(lib, f, x, xt, n, d, ldx, w, wt, r, ldw, act, g, ldg, y, yt, ldy, None)
 
+    # only calls that fail validation (or have nothing to do) are made here:
+    # a call that passes would launch on made-up addresses
     assert l(n=0) == 0 and l(r=0) == 0
-    assert l(n=-1) == 1 and l(act=2) == 1 and l(yt=9) == 1
+    assert l(n=-1) == 1 and l(act=2) == 1 and l(yt=9) == 1 and l(wt=7) == 1
     assert l(xt=0) == 2                           # fp32 activations
+    assert l(wt=2) == 2                           # 16-bit weights of another type than X
     assert l(d=100, ldx=100, ldw=100) == 5 and l(d=0) == 5
     assert l(ldx=200) == 3 and l(ldw=128) == 3 and l(ldy=32) == 3
     assert l(act=1, g=G, ldg=32) == 3
     assert l(x=None) == 1 and l(w=None) == 1 and l(y=None) == 1 and l(act=1, ldg=64) == 1
     assert l(x=C.c_void_p(0x10008)) == 4 and l(ldx=260) == 4 and l(ldw=258) == 4
+    assert l(wt=1, ldw=260) == 4                  # 16-bit weights: rows on 16 bytes
+    assert l(wt=1, ldx=1 << 22, ldw=256) == 5     # 16-bit weights: strides below 2^22
     assert l(y=C.c_void_p(0x10000 + 512)) == 1    # Y inside X
-    assert l(act=1, g=G, ldg=64, y=G, yt=1, ldy=64) != 1 or True   # Y == G allowed (not launched here)
     assert l(act=1, g=G, ldg=64, y=C.c_void_p(0x80000000 + 2), yt=1, ldy=64) == 1
+
+
+def test_round16_argument_errors(lib):
+    f = "gptq_round16"
+    S, D = ALIGNED, C.c_void_p(0x40000000)
+
+    def r(s=S, rows=4, cols=64, lds=64, dt=1, d=D, ldd=64):
+        return _st(lib, f, s, rows, cols, lds, dt, d, ldd, None)
+
+    assert r(rows=0) == 0 and r(cols=0) == 0
+    assert r(rows=-1) == 1 and r(dt=5) == 1
+    assert r(dt=0) == 2
+    assert r(lds=32) == 3 and r(ldd=32) == 3
+    assert r(s=None) == 1 and r(d=None) == 1
+    assert r(s=C.c_void_p(0x10002)) == 4 and r(d=C.c_void_p(0x40000001)) == 4
+    assert r(d=C.c_void_p(0x10000 + 64)) == 1     # dst inside src
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -78,18 +78,80 @@ FWD = [
 ]
 
 
+@pytest.mark.parametrize("w16", [False, True], ids=["w_f32", "w_16bit"])
 @pytest.mark.parametrize("n,d,r,xdt,ydt,gated", FWD)
-def test_linear_forward_matches_oracle(n, d, r, xdt, ydt, gated):
+def test_linear_forward_matches_oracle(n, d, r, xdt, ydt, gated, w16):
+    """fp32 weights (rounded inside the call) and weights rounded beforehand
+    by round16 (the LDS-direct path) against the oracle forward."""
     import post_weight_quantization_23_amd as q
-    print(f"\n[forward] {n}x{d} -> {r} {xdt}->{ydt} gated={gated}", flush=True)
+    print(f"\n[forward] {n}x{d} -> {r} {xdt}->{ydt} gated={gated} w16={w16}", flush=True)
     X = S.activations_host(n, d, "t4", max(1, d // 50), 10.0, wid=90 + n % 13, dtype=xdt)
     W = S.weights_host(r, d, wid=91 + r % 11, dtype="float32", std=0.05)
     G = S.activations_host(n, r, "t4", 0, 1.0, wid=92, dtype=xdt) if gated else None
     Xd = torch.from_numpy(X).cuda().to(DT[xdt])
     Gd = torch.from_numpy(G).cuda().to(DT[xdt]) if gated else None
-    Y = q.linear_forward(Xd, torch.from_numpy(W).cuda(), gate=Gd, out_dtype=DT[ydt])
+    Wd = torch.from_numpy(W).cuda()
+    if w16:
+        Wd = q.round16(Wd, DT[xdt])
+    Y = q.linear_forward(Xd, Wd, gate=Gd, out_dtype=DT[ydt])
     torch.cuda.synchronize()
     check_forward(Y.double().cpu().numpy(), X, W, xdt, ydt, G)
+
+
+@pytest.mark.parametrize("n,d,r,xdt,gated", [(700, 256, 600, "bfloat16", True), (515, 192, 300, "float16", False),
+                                             (1100, 128, 1030, "bfloat16", False)])
+def test_linear_forward_weight_paths_agree_bitwise(n, d, r, xdt, gated):
+    """The register path (fp32 weights) and the LDS-direct path (16-bit
+    weights) give the MFMAs the same operands in the same order."""
+    import post_weight_quantization_23_amd as q
+    X = torch.from_numpy(S.activations_host(n, d, "t4", 4, 10.0, wid=97, dtype=xdt)).cuda().to(DT[xdt])
+    W = torch.from_numpy(S.weights_host(r, d, wid=98, dtype="float32", std=0.05)).cuda()
+    G = torch.from_numpy(S.activations_host(n, r, "t4", 0, 1.0, wid=99, dtype=xdt)).cuda().to(DT[xdt]) if gated \
+        else None
+    Ya = q.linear_forward(X, W, gate=G, out_dtype=torch.float32)
+    Yb = q.linear_forward(X, q.round16(W, DT[xdt]), gate=G, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(Ya, Yb)
+
+
+@pytest.mark.parametrize("dt", ["bfloat16", "float16"])
+def test_round16_matches_oracle(dt):
+    """Element-wise rounding against the oracle's, bit for bit: random values
+    over many binades, exact midpoints (ties to even), subnormal results,
+    overflow to infinity and signed zeros; a strided, unaligned view takes the
+    element-wise path."""
+    import post_weight_quantization_23_amd as q
+    rng = np.random.default_rng(21)
+    mant = {"bfloat16": 7, "float16": 10}[dt]
+    vals = [rng.standard_normal(3000) * np.exp2(rng.integers(-30, 30, 3000))]
+    k = rng.integers(1, 1 << mant, 500).astype(np.float64)          # midpoints k + 1/2 at the 16-bit spacing
+    vals.append((1.0 + (k + 0.5) / (1 << mant)) * np.exp2(rng.integers(-10, 10, 500)))
+    if dt == "float16":
+        vals.append(rng.uniform(1e-8, 6e-5, 300))                      # subnormal results
+        vals.append(np.array([65504.0, 65519.0, 65520.0, 70000.0, 1e30]))  # around the largest fp16
+    else:
+        vals.append(np.array([3.3895e38, 3.39e38, 3.4e38, 1e-39, 1e-41]))
+    v = np.concatenate(vals + [np.array([0.0, -0.0])])
+    v = np.concatenate([v, -v]).astype(np.float32)
+    rows, cols = 6, (v.size + 5) // 6
+    A = np.zeros((rows, cols), np.float32)
+    A.reshape(-1)[:v.size] = v
+    exp = ref.round16(A.astype(np.float64), dt)
+    Ad = torch.from_numpy(A).cuda()
+    got = q.round16(Ad, DT[dt]).double().cpu().numpy()
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(exp))
+    np.testing.assert_array_equal(got, exp)
+    wide = torch.zeros((rows, cols + 3), dtype=torch.float32, device="cuda")
+    wide[:, 1:1 + cols] = Ad
+    out = torch.zeros((rows, cols + 5), dtype=DT[dt], device="cuda")
+    q.round16(wide[:, 1:1 + cols], DT[dt], out=out[:, 1:1 + cols])
+    got2 = out.double().cpu().numpy()
+    np.testing.assert_array_equal(got2[:, 1:1 + cols], exp)
+    assert np.all(got2[:, 0] == 0) and np.all(got2[:, 1 + cols:] == 0)
+    # IEEE fixes the non-finite cases: infinities stay, NaN stays NaN
+    sp = torch.tensor([[np.inf, -np.inf, np.nan, 1.0]], dtype=torch.float32, device="cuda")
+    r16 = q.round16(sp, DT[dt]).float().cpu().numpy()[0]
+    assert r16[0] == np.inf and r16[1] == -np.inf and np.isnan(r16[2]) and r16[3] == 1.0
 
 
 def test_linear_forward_gate_in_place():
@@ -107,13 +169,14 @@ def test_linear_forward_gate_in_place():
 
 def test_linear_forward_full_size_sampled():
     """The benchmark's activations (262144 x 4096 bf16) through an up-projection
-    shaped layer (11008 x 4096), bf16 out, checked on sampled tokens."""
+    shaped layer (11008 x 4096, weights rounded by round16 as the layer-by-layer
+    pass does), bf16 out, checked on sampled tokens."""
     import post_weight_quantization_23_amd as q
     w = S.WORKLOADS["llama7b_attn_4096x4096"]
     print(f"\n[forward full] {w.tokens}x{w.cols} -> 11008", flush=True)
     _, X = S.workload_device(w, device="cuda")
     Wd = S.weights_device(11008, w.cols, 96, 0, "float32", device="cuda")
-    Y = q.linear_forward(X, Wd)
+    Y = q.linear_forward(X, q.round16(Wd, X.dtype))
     torch.cuda.synchronize()
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([[0, w.tokens - 1], rng.choice(w.tokens, 14, replace=False)]))
