@@ -60,7 +60,9 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), "-shared", "--offload-arch=gfx950", "-fPIC", "-o", tmp, *objs]
+    # --no-undefined: a kernel the host pass failed to instantiate must fail the
+    # build here, not the load of the library
+    cmd = [hipcc(), "-shared", "--offload-arch=gfx950", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -22,6 +22,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace gptq {
 
@@ -232,6 +233,191 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmPair pr) {
     }
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// The same product with the operands carried from memory straight into LDS
+// by buffer loads that write LDS (16 bytes per lane), one K-step ahead, when
+// both operands are 16-byte aligned with ld % 4 == 0 (and ld < 2^22).  The
+// LDS tiles are plain copies of the operand rows as they lie in memory --
+// A[m][k] rows (a_trans == 0) or A^T [k][m] rows, B[k][n] rows (b_trans == 0)
+// or B^T [n][k] rows -- and each MFMA operand is read with the matching
+// strides.  Masked (triangular) elements and k >= K are replaced by zero as
+// they are read, whatever LDS holds; rows past the end of an operand load
+// zeros from the descriptor bounds, and columns past M or N only reach
+// outputs that are not stored.  The operands and their order are those of
+// gemm_f32_kernel, so both kernels give the same bits.
+GPTQ_DEV int kswz(int r) { return (r >> 1) & 7; }
+
+// The K-loop of gemm_f32_dma_kernel (a device function, so that the
+// LDS-direct loads are compiled for the device only).
+template <int TM, int TN, int KT>
+GPTQ_DEV void gemm_steps_dma(const GemmArgs& g, int m0, int n0, int k_lo, int k_hi, int wm, int wn,
+                             floatx16 (&acc)[TM / 64][TN / 64]) {
+  constexpr int MB = TM / 64, NB = TN / 64;
+  constexpr int ABYTES = TM * KT * 4, BBYTES = TN * KT * 4, BUF = ABYTES + BBYTES;
+  constexpr int NIA = ABYTES / 4096, NIB = BBYTES / 4096;  // load instructions per wave and step
+  static_assert(NIA * 4096 == ABYTES && NIB * 4096 == BBYTES, "whole load instructions");
+  static_assert(KT == 32, "rows along k are 8 chunks");
+  extern __shared__ __attribute__((aligned(16))) float gemm_smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool ak = !g.a_trans, bk = g.b_trans != 0;  // rows run along k
+  const int rowa = ak ? KT * 4 : TM * 4, rowb = bk ? KT * 4 : TN * 4;  // bytes per LDS row
+  // Byte offset (from the step's tile origin in memory) of the chunk each
+  // lane carries: LDS byte I * 1024 + 16 lane is row byte / row_bytes,
+  // 16-byte position p of it.  Rows along k (8 chunks) hold chunk c at
+  // position c ^ kswz(row), so that the 32 rows an operand read touches at
+  // one k spread over 16 banks; rows along m or n are read contiguously and
+  // are not swizzled.
+  int offa[NIA], offb[NIB];
+#pragma unroll
+  for (int q = 0; q < NIA; ++q) {
+    const int byte = (wave * NIA + q) * 1024 + 16 * lane, r = byte / rowa, p = (byte % rowa) >> 4;
+    offa[q] = r * (int)g.lda * 4 + 16 * (ak ? p ^ kswz(r) : p);
+  }
+#pragma unroll
+  for (int q = 0; q < NIB; ++q) {
+    const int byte = (wave * NIB + q) * 1024 + 16 * lane, r = byte / rowb, p = (byte % rowb) >> 4;
+    offb[q] = r * (int)g.ldb * 4 + 16 * (bk ? p ^ kswz(r) : p);
+  }
+  lds_u8* lbase = (lds_u8*)gemm_smem;  // generic to LDS address space
+  auto dma = [&](int k0, int b) {
+    // tile origin, rows that exist from it, and its column offset in a row
+    const float* ab = ak ? g.A + (int64_t)m0 * g.lda + k0 : g.A + (int64_t)k0 * g.lda + m0;
+    const int ar = ak ? min(g.M - m0, TM) : min(g.K - k0, KT), ac = ak ? k0 : m0;
+    const float* bb = bk ? g.B + (int64_t)n0 * g.ldb + k0 : g.B + (int64_t)k0 * g.ldb + n0;
+    const int br = bk ? min(g.N - n0, TN) : min(g.K - k0, KT), bc = bk ? k0 : n0;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)ab, (short)0, (int)((int64_t)ar * g.lda * 4 - (int64_t)ac * 4), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)bb, (short)0, (int)((int64_t)br * g.ldb * 4 - (int64_t)bc * 4), 0x00020000);
+#pragma unroll
+    for (int q = 0; q < NIA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lbase + b * BUF + (wave * NIA + q) * 1024, 16, offa[q], 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NIB; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, lbase + b * BUF + ABYTES + (wave * NIB + q) * 1024, 16, offb[q],
+                                               0, 0, 0);
+  };
+
+  if (k_lo < k_hi) {
+    dma(k_lo, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = k_lo; k0 < k_hi; k0 += KT) {
+      if (k0 + KT < k_hi) dma(k0 + KT, buf ^ 1);
+      const float* as = gemm_smem + buf * (BUF / 4);
+      const float* bs = as + ABYTES / 4;
+      // Masks and the K tail only matter on steps that cross a triangle's
+      // diagonal or the end of K (a uniform test); other steps read plainly.
+      bool plain = k0 + KT <= g.K;
+      if (g.a_mask == MASK_UPPER) plain = plain && k0 + g.a_off >= m0 + TM - 1;
+      if (g.a_mask == MASK_LOWER) plain = plain && m0 + g.a_off >= k0 + KT - 1;
+      if (g.b_mask == MASK_UPPER) plain = plain && n0 + g.b_off >= k0 + KT - 1;
+      if (g.b_mask == MASK_LOWER) plain = plain && k0 + g.b_off >= n0 + TN - 1;
+      auto step = [&](auto masked) {
+#pragma unroll
+        for (int kk = 0; kk < KT / 2; ++kk) {
+          const int k = 2 * kk + (lane >> 5), gk = k0 + k;
+          float a[MB], b[NB];
+#pragma unroll
+          for (int i = 0; i < MB; ++i) {
+            const int m = wm + 32 * i + (lane & 31);
+            a[i] = ak ? as[m * KT + ((((k >> 2) ^ kswz(m))) << 2) + (k & 3)] : as[k * TM + m];
+            if constexpr (decltype(masked)::value) {
+              // branch-free: the value is read, then replaced by zero
+              const int gm = m0 + m;
+              const bool keep = gk < g.K && (g.a_mask == MASK_UPPER   ? gk + g.a_off >= gm
+                                             : g.a_mask == MASK_LOWER ? gm + g.a_off >= gk
+                                                                      : true);
+              a[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a[i]) & (0u - (uint32_t)keep));
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int n = wn + 32 * j + (lane & 31);
+            b[j] = bk ? bs[n * KT + ((((k >> 2) ^ kswz(n))) << 2) + (k & 3)] : bs[k * TN + n];
+            if constexpr (decltype(masked)::value) {
+              const int gn = n0 + n;
+              const bool keep = gk < g.K && (g.b_mask == MASK_UPPER   ? gn + g.b_off >= gk
+                                             : g.b_mask == MASK_LOWER ? gk + g.b_off >= gn
+                                                                      : true);
+              b[j] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b[j]) & (0u - (uint32_t)keep));
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+      };
+      if (plain) step(std::false_type{});
+      else step(std::true_type{});
+      // step k0 + KT has landed (own loads) in every wave (barrier); buffer
+      // buf is free for the step after it
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+}
+
+template <int TM, int TN, int KT>
+__global__ __launch_bounds__(256) void gemm_f32_dma_kernel(GemmPair pr) {
+  constexpr int WM = TM / 2, WN = TN / 2;
+  constexpr int MB = WM / 32, NB = WN / 32;
+
+  const bool second = (int)blockIdx.x >= pr.tiles0;
+  const GemmArgs& g = second ? pr.g[1] : pr.g[0];
+  const int bid = second ? (int)blockIdx.x - pr.tiles0 : (int)blockIdx.x;
+  const int tiles_n = (g.N + TN - 1) / TN;
+  const int bm = bid / tiles_n, bn = bid % tiles_n;
+  const int m0 = bm * TM, n0 = bn * TN;
+  if (g.upper_only && n0 + TN <= m0) return;  // tile strictly below the diagonal
+
+  int k_lo = 0, k_hi = g.K;
+  if (g.a_mask == MASK_UPPER) k_lo = max(k_lo, m0 - g.a_off);
+  if (g.a_mask == MASK_LOWER) k_hi = min(k_hi, m0 + TM + g.a_off);
+  if (g.b_mask == MASK_UPPER) k_hi = min(k_hi, n0 + TN + g.b_off);
+  if (g.b_mask == MASK_LOWER) k_lo = max(k_lo, n0 - g.b_off);
+  k_lo = (k_lo / KT) * KT;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+
+  floatx16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  gemm_steps_dma<TM, TN, KT>(g, m0, n0, k_lo, k_hi, wm, wn, acc);
+
+  // ---- epilogue: lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] ----
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int col = n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < g.M && col < g.N) {
+          float* p = g.C + (int64_t)row * g.ldc + col;
+          float out = g.alpha * acc[i][j][v];
+          if (g.beta != 0.f) out = __builtin_fmaf(g.beta, *p, out);
+          *p = out;
+        }
+      }
+    }
+}
+
 // Small products (few 64 x 64 tiles, K <= 512): 32 x 32 output tiles, the
 // workgroup's 4 waves split K four ways and load all their operands straight
 // into registers at once (one memory latency instead of one per K-step), then
@@ -326,15 +512,18 @@ int64_t tiles_of(const GemmArgs& g) {
   return (g.M <= 0 || g.N <= 0) ? 0 : (int64_t)((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
 }
 
+// Operands the LDS-direct kernel can take: 16-byte aligned, rows of a whole
+// number of 16-byte chunks, and every byte offset inside a tile's rows below
+// 2^31 (ld < 2^22 floats).
+bool dma_ok(const GemmArgs& g) {
+  auto ok = [](const float* p, int64_t ld) {
+    return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 3) == 0 && ld < (int64_t(1) << 22);
+  };
+  return ok(g.A, g.lda) && ok(g.B, g.ldb);
+}
+
 template <int TM, int TN, int KT>
 void launch_tile(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
-  constexpr size_t smem = (size_t)2 * KT * ((TM + PAD) + (TN + PAD)) * sizeof(float);
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)gemm_f32_kernel<TM, TN, KT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)smem);
-    attr = true;
-  }
   GemmPair pr;
   pr.g[0] = g0;
   pr.g[1] = g1 ? *g1 : g0;
@@ -342,6 +531,24 @@ void launch_tile(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
   const int64_t t1 = g1 ? tiles_of<TM, TN, KT>(*g1) : 0;
   pr.tiles0 = (int)t0;
   if (t0 + t1 == 0) return;
+  if (dma_ok(g0) && (!g1 || dma_ok(*g1))) {
+    constexpr size_t smem = (size_t)2 * KT * (TM + TN) * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)gemm_f32_dma_kernel<TM, TN, KT>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+      attr = true;
+    }
+    hipLaunchKernelGGL((gemm_f32_dma_kernel<TM, TN, KT>), dim3((unsigned)(t0 + t1)), dim3(256), smem, s, pr);
+    return;
+  }
+  constexpr size_t smem = (size_t)2 * KT * ((TM + PAD) + (TN + PAD)) * sizeof(float);
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)gemm_f32_kernel<TM, TN, KT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)smem);
+    attr = true;
+  }
   hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, KT>), dim3((unsigned)(t0 + t1)), dim3(256), smem, s, pr);
 }
 
