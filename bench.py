@@ -480,6 +480,85 @@ def bench_stack(args) -> int:
     return 0
 
 
+GRID_VARIANTS = [
+    # name, bits, groupsize, symmetric
+    ("asym_b4_g128", 4, 128, False),
+    ("sym_b4_g128", 4, 128, True),
+    ("asym_b2_g128", 2, 128, False),
+    ("asym_b3_g128", 3, 128, False),
+    ("asym_b8_g128", 8, 128, False),
+    ("asym_b4_g64", 4, 64, False),
+    ("asym_b4_g32", 4, 32, False),
+    ("asym_b4_row", 4, -1, False),
+]
+
+
+def bench_grid(args) -> int:
+    """The quantize stage (ruler fits, the column loop with its block repairs
+    and the deferred products) on the 4096 x 4096 layer for every grid
+    variant, on one factor U of that layer's Hessian."""
+    import torch
+
+    from post_weight_quantization_23_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_23_amd import build as b
+        b.build()
+    import post_weight_quantization_23_amd as q
+    from synth import inputs as S
+
+    w = S.WORKLOADS["llama7b_attn_4096x4096"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W, X = S.workload_device(w, device=dev)
+    r, c = w.rows, w.cols
+    U = torch.zeros((c, c), dtype=torch.float32, device=dev)
+    q.hessian_accumulate(U, X)
+    perm, dead, _ = q.prepare(U, w.percdamp, False)
+    del X
+    ws = q.Workspace()
+    res = {}
+    steps = max(1, args.steps)
+    for name, bits, gs, sym in GRID_VARIANTS:
+        def one():
+            return q.quantize_layer(W, U, perm, dead, bits=bits, groupsize=gs, blocksize=w.blocksize, ws=ws,
+                                    sym=sym)
+        for _ in range(max(1, args.warmup)):
+            one()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            one()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"bits": bits, "groupsize": gs, "sym": sym, "ms": e0.elapsed_time(e1) / steps}
+        log(f"{name}: {res[name]['ms']:.3f} ms")
+    # the column loop's repairs: every column updates all later columns of
+    # every row, r * c (c - 1) / 2 multiply-adds, however they are blocked
+    flops = float(r) * c * (c - 1)
+    tot_ms = sum(v["ms"] for v in res.values())
+    worst = max(res.values(), key=lambda v: v["ms"])
+    for v in res.values():
+        v["weights_per_s"] = r * c / (v["ms"] * 1e-3)
+    ach = flops / (worst["ms"] * 1e-3) / 1e12
+    rec = {
+        "metric": "GPTQ quantize stage per grid variant on 4096x4096 (ruler fits, column loop, deferred "
+                  "products): weights/s over all variants",
+        "value": len(res) * r * c / (tot_ms * 1e-3), "unit": "weights/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": tot_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0, 0.02^2) weights; U from the Hessian of Student-t(4) activations)",
+        "config": {"workload": "llama7b_attn_4096x4096_grid_variants", "rows": r, "cols": c,
+                   "blocksize": w.blocksize, "variants": res},
+        "roofline": {"kernel": "gptq_quantize_layer, slowest variant (HIP events around the call)", "bound": "mfma",
+                     "achieved": ach, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_FP32_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +571,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gemv-model", default="llama7b", choices=sorted(GEMV_MODELS))
     ap.add_argument("--hadamard", action="store_true")
     ap.add_argument("--stack", action="store_true")
+    ap.add_argument("--grid", action="store_true")
     ap.add_argument("--blocks", type=int, default=2)
     args = ap.parse_args(argv)
 
@@ -511,6 +591,8 @@ def main(argv=None) -> int:
         return bench_hadamard(args)
     if args.stack:
         return bench_stack(args)
+    if args.grid:
+        return bench_grid(args)
 
     from post_weight_quantization_23_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):

@@ -137,6 +137,25 @@ def test_hessian_matches_oracle(xdtype, n, d, batches, pad):
     check_h(H, ref.hessian(X))
 
 
+@pytest.mark.parametrize("n,d", [(3000, 520), (1500, 1024)])
+def test_hessian_fp32_data_paths_agree_bitwise(n, d):
+    """fp32 X runs the fp32 MFMA product: 16-byte aligned operands go through
+    the LDS-direct kernel, X shifted by one element through the register
+    kernel; same operands, same k pairing, so the Hessians are bitwise equal
+    (and match the oracle)."""
+    X = S.activations_host(n, d, "t4", outliers=4, gain=20.0, wid=59, dtype="float32")
+    Xa = to_dev(X, torch.float32)
+    shifted = torch.zeros((n, d + 4), dtype=torch.float32, device="cuda")
+    shifted[:, 1:1 + d] = Xa
+    Ha = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+    Hb = torch.zeros_like(Ha)
+    gq().hessian_accumulate(Ha, Xa)
+    gq().hessian_accumulate(Hb, shifted[:, 1:1 + d])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.triu(Ha), torch.triu(Hb))
+    check_h(Ha, ref.hessian(X))
+
+
 @pytest.mark.parametrize("ldx", [(1 << 24) - 64, (1 << 24) + 64])
 def test_hessian_huge_row_stride(ldx):
     """Row strides at the limit of the interior-tile path (64 token rows of one
