@@ -22,7 +22,9 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libgptq_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["gptq_api.hip", "gemm_f32.hip", "syrk.hip", "prepare.hip", "quantize.hip", "pack.hip", "gemv.hip", "hadamard.hip", "linear.hip"]
+# slowest first: the pool starts them at once
+SOURCES = ["quantize.hip", "linear.hip", "gemm_f32.hip", "syrk.hip", "gemv.hip", "prepare.hip",
+           "hadamard.hip", "pack.hip", "gptq_api.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

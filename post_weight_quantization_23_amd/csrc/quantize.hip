@@ -310,13 +310,13 @@ GPTQ_DEV void block_ruler(const BlockArgs& a, const float (&w)[S], int p, int64_
 // The block's columns in order, for the L lanes of each row (see the file
 // header for the lane mapping).  On return w[m] holds, for every column of
 // the block, its value when its turn came (V's zero diagonal leaves it
-// alone afterwards).  With MIDGROUPS the ruler changes inside the block, so
+// alone afterwards).  With MIDG != 0 the ruler changes inside the block, so
 // the tick offset, w_hat and error of each column are recorded as they are
 // taken, and the fast pass's doubtful decisions are collected per step;
 // otherwise everything is recomputed from w after the loop.  EXACT == false
 // decides with t = x * (1/scale); an unflagged fast pass is bitwise the exact
 // pass, because every later value depends on the decision only.
-template <int L, bool MIDGROUPS, bool FULL, bool EXACT>
+template <int L, int MIDG, bool FULL, bool EXACT>
 GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row, bool valid,
                         const float* Wrow, float (&w)[BMAX / L], float (&qreg)[BMAX / L],
                         float (&ereg)[BMAX / L], float (&whreg)[BMAX / L], float& scale, float& zero) {
@@ -329,7 +329,7 @@ GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row,
   float y = __fdiv_rn(1.0f, scale);
   float lo = -zero, hi = maxq - zero;
   uint64_t bad = 0;
-  int next_group = MIDGROUPS ? (int)g : BMAX;
+  int next_group = MIDG != 0 ? (int)g : BMAX;
   // Lanes of the rows' owners of block column j: lane j % L of every row.
   constexpr uint64_t OWN0 = L == 16 ? 0x0001000100010001ull : 0x1111111111111111ull;
 
@@ -352,8 +352,14 @@ GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row,
     // A short block runs all BMAX steps: its missing columns hold 0 in w and
     // in V, quantize to an error of exactly 0 and are never stored.
     const int mj = j / L, pj = j % L;
-    if constexpr (MIDGROUPS) {
-      if (j > 0 && j == next_group && (FULL || j < Bw)) {
+    // A refit can happen at step j only where a group may start: with
+    // MIDG == 32 at multiples of 32, so the refit code exists at those steps
+    // only (with any width it is copied into every step of the unrolled loop,
+    // far beyond the instruction cache).  j is a constant in each unrolled
+    // step, so the test folds away.
+    const bool can_refit = MIDG == 32 ? (j > 0 && j % 32 == 0) : (MIDG != 0 && j > 0);
+    if (can_refit) {
+      if (j == next_group && (FULL || j < Bw)) {
         fit_group<L, S>(w, p, j, Bw, g, i1, c, Wrow, valid, maxq, a.sym != 0, scale, zero);
         y = __fdiv_rn(1.0f, scale);
         lo = -zero;
@@ -369,7 +375,7 @@ GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row,
     const float x = w[mj];
     const float dq = tick<EXACT>(x, scale, y, lo, hi);
     const float err = __builtin_fmaf(-scale, dq, x);   // w - scale * (q - zero)
-    if constexpr (MIDGROUPS) {
+    if constexpr (MIDG != 0) {
       const bool own = (p == pj);
       qreg[mj] = own ? dq + zero : qreg[mj];
       whreg[mj] = own ? __fmul_rn(scale, dq) : whreg[mj];
@@ -393,9 +399,10 @@ GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row,
   return bad != 0;
 }
 
-// MIDGROUPS: groups shorter than the block also start inside it.  FULL: the
+// MIDG: groups shorter than the block also start inside it (32: their width
+// is a multiple of 32; -1: any width; 0: none).  FULL: the
 // block has all BMAX columns.
-template <int L, bool MIDGROUPS, bool FULL>
+template <int L, int MIDG, bool FULL>
 __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   constexpr int S = BMAX / L;          // slots per lane
   constexpr int ROWS = 256 / L;        // rows per workgroup
@@ -426,8 +433,8 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
 #pragma unroll
   for (int m = 0; m < S; ++m) qreg[m] = ereg[m] = whreg[m] = 0.f;
   float scale = 1.f, zero = 0.f;
-  bool bad = run_chain<L, MIDGROUPS, FULL, false>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
-  if constexpr (!MIDGROUPS) {
+  bool bad = run_chain<L, MIDG, FULL, false>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
+  if constexpr (MIDG == 0) {
     const float y = __fdiv_rn(1.0f, scale);
 #pragma unroll
     for (int m = 0; m < S; ++m) bad = bad || near_half(w[m], y);
@@ -435,9 +442,9 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   const bool exact = __ballot(bad) != 0;   // wave-uniform
   if (exact) {                              // repeat this wave's rows exactly
     load_w();
-    run_chain<L, MIDGROUPS, FULL, true>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
+    run_chain<L, MIDG, FULL, true>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
   }
-  if constexpr (!MIDGROUPS) {
+  if constexpr (MIDG == 0) {
     // Codes, w_hat and errors from the values the columns had at their turn.
     const float y = __fdiv_rn(1.0f, scale);
     const float lo = -zero, hi = maxq - zero;
@@ -554,7 +561,8 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   b.lde = SB;
   // 16 lanes per row when there are enough rows to fill the chip that way.
   const bool wide = r * 16 >= 256 * 64;
-  const bool mid = a.groupsize > 0 && a.groupsize < B;
+  // groups shorter than the block: width a multiple of 32 (32), any (-1)
+  const int midg = !(a.groupsize > 0 && a.groupsize < B) ? 0 : (a.groupsize % 32 == 0) ? 32 : -1;
   const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
   for (int64_t s1 = 0; s1 < c; s1 += SB) {
     const int64_t s2 = std::min(s1 + SB, c);
@@ -566,13 +574,19 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
       b.E = E + (i1 - s1);
       const bool full = Bw == BMAX;
 #define GPTQ_BLOCK(LL, MID, FU, G) hipLaunchKernelGGL((block_kernel<LL, MID, FU>), G, dim3(256), 0, s, b)
+#define GPTQ_BLOCK_F(LL, MID, G) \
+  do { if (full) GPTQ_BLOCK(LL, MID, true, G); else GPTQ_BLOCK(LL, MID, false, G); } while (0)
+      // Widths that are multiples of 32 have their own variant in the
+      // 16-lane kernel (layers of 1024 rows and more); otherwise any width.
       if (wide) {
-        if (mid) { if (full) GPTQ_BLOCK(16, true, true, g16); else GPTQ_BLOCK(16, true, false, g16); }
-        else     { if (full) GPTQ_BLOCK(16, false, true, g16); else GPTQ_BLOCK(16, false, false, g16); }
+        if (midg == 0) GPTQ_BLOCK_F(16, 0, g16);
+        else if (midg == 32) GPTQ_BLOCK_F(16, 32, g16);
+        else GPTQ_BLOCK_F(16, -1, g16);
       } else {
-        if (mid) { if (full) GPTQ_BLOCK(4, true, true, g4); else GPTQ_BLOCK(4, true, false, g4); }
-        else     { if (full) GPTQ_BLOCK(4, false, true, g4); else GPTQ_BLOCK(4, false, false, g4); }
+        if (midg == 0) GPTQ_BLOCK_F(4, 0, g4);
+        else GPTQ_BLOCK_F(4, -1, g4);
       }
+#undef GPTQ_BLOCK_F
 #undef GPTQ_BLOCK
       // repairs of this block's errors to the rest of the super-block, at once
       if (i2 < s2) gemm_update(s, r, c, b.E, SB, Bw, a.U, i1, i2, s2, Wp);

@@ -236,6 +236,8 @@ CASES = [
     (40, 160, 8, -1, 32, False, 0, "float32"),
     (1100, 256, 4, 128, 128, False, 0, "bfloat16"),  # 16 lanes per row path
     (1024, 320, 3, 32, 64, True, 1, "bfloat16"),     # 16 lanes, groups inside blocks
+    (1100, 384, 4, 64, 128, True, 1, "bfloat16"),    # 16 lanes, two groups per full block
+    (1040, 256, 4, 32, 128, False, 2, "float16"),    # 16 lanes, four groups per full block
     (20, 300, 4, 256, 128, False, 0, "float32"),     # group spanning two blocks
     (1030, 1100, 4, 128, 128, True, 2, "bfloat16"),  # several super-blocks, ragged tail
     (70, 1300, 3, 256, 64, False, 0, "float16"),     # groups of 4 blocks across super-blocks
