@@ -29,7 +29,7 @@ Sources (the pages are cited by title and section):
   group size 128/64/32, act-order.
 * apxml course chapter "intro-gptq": the layer objective ||W X - W_q X||^2.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 
 * H is the raw 2 * sum_t x_t x_t^T, never rescaled to a running mean (the
   pages call the two the same matrix up to a harmless constant factor).
