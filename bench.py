@@ -50,6 +50,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_syrk16_{workload}.json")
 SYRK_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "syrk.hip")
 GEMV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_{workload}.json")
 GEMV_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "gemv.hip")
+LINEAR_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_linear_{workload}.json")
+LINEAR_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "linear.hip")
 HADAMARD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_hadamard_{workload}.json")
 HADAMARD_SOURCE = os.path.join(ROOT, "post_weight_quantization_23_amd", "csrc", "hadamard.hip")
 
@@ -472,7 +474,9 @@ def bench_stack(args) -> int:
         "roofline": {"kernel": "linear_kernel<bf16, 16-bit weights> (quantized forward 262144 x 4096 -> 11008, "
                                "HIP events)",
                      "bound": "mfma", "achieved": tfl, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tfl / PEAK_BF16_TFLOPS, "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "frac": tfl / PEAK_BF16_TFLOPS,
+                     "traffic": load_traffic("llama7b_mlp_forward_262144x4096x11008", LINEAR_TRAFFIC_FILE, LINEAR_SOURCE),
+                     "algorithmic_flops_per_launch": flops,
                      "ms_per_launch": fwd_ms, "ms_per_launch_fp32_weights": fwd_f32_ms},
         "cpu_baseline": None,
     }
