@@ -273,7 +273,8 @@ gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int
   if (wt != GPTQ_F32 && wt != xt) return fail(GPTQ_EDTYPE, fn, "W_hat must be GPTQ_F32 or of X's type");
   if (act != 0 && act != 1) return fail(GPTQ_EINVAL, fn, "act must be 0 (none) or 1 (silu(G) * up)");
   if (d < 64 || d % 64 != 0) return fail(GPTQ_EUNSUPPORTED, fn, "d must be a positive multiple of 64");
-  if (r > (int64_t)INT_MAX / 2 || d > (int64_t)INT_MAX / 2 || n_tok > kMaxRows)
+  if (r > (int64_t)INT_MAX / 2 || d > (int64_t)INT_MAX / 2 || n_tok > kMaxRows ||
+      ((n_tok + 255) / 256) * ((r + 255) / 256) >= (int64_t)INT_MAX)   // one workgroup per 256 x 256 tile
     return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
   if (n_tok == 0 || r == 0) return ok();
   if (ldx < d || ldw < d || ldy < r || (act == 1 && ldg < r)) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");

@@ -191,6 +191,7 @@ def test_linear_forward_argument_errors(lib):
     assert l(x=C.c_void_p(0x10008)) == 4 and l(ldx=260) == 4 and l(ldw=258) == 4
     assert l(wt=1, ldw=260) == 4                  # 16-bit weights: rows on 16 bytes
     assert l(wt=1, ldx=1 << 22, ldw=256) == 5     # 16-bit weights: strides below 2^22
+    assert l(n=1 << 29, r=1 << 29, ldy=1 << 29) == 5   # more 256 x 256 tiles than a grid holds
     assert l(y=C.c_void_p(0x10000 + 512)) == 1    # Y inside X
     assert l(act=1, g=G, ldg=64, y=C.c_void_p(0x80000000 + 2), yt=1, ldy=64) == 1
 
