@@ -347,7 +347,13 @@ def test_dead_inputs_zeroed_and_per_row_ruler_sees_original():
 
 
 # --- tie replay adjudication ---
-def test_tie_replay_adopts_only_near_ties():
+# The parity procedure: at a near-tie (the pre-rounding value within 1e-3 of a
+# tick midpoint) both neighbouring ticks are the nearest tick up to rounding
+# order ("What quantization is, and why anyone bothers": each weight goes to
+# its nearest tick), so another implementation's choice of the other
+# neighbour is adopted; anything else is a hard mismatch.  These pins build
+# the pre-rounding values by hand, so every branch asserts something.
+def test_tie_replay_identical_codes_change_nothing():
     rng = np.random.default_rng(19)
     r, c = 6, 32
     X = _correlated_x(rng, 100, c)
@@ -357,16 +363,115 @@ def test_tie_replay_adopts_only_near_ties():
     same = ref.TieReplay(base["codes_proc"], base["zeros"])
     again = ref.gptq_quantize(W0, H, bits=4, replay=same)
     assert same.hard == 0 and same.near_ties == 0
+    assert same.zero_hard == 0 and same.zero_near_ties == 0
     np.testing.assert_array_equal(again["codes"], base["codes"])
-    # Shift one code far from any midpoint: counted as hard, not adopted.
-    bad = base["codes_proc"].copy()
-    j = 5
-    t = base["pre_round"][2, j] / base["scales"][2, 0]
-    if abs(t - np.floor(t) - 0.5) > 0.01:
-        bad[2, j] = (bad[2, j] + 3) % 16
-        rep = ref.TieReplay(bad, base["zeros"])
-        ref.gptq_quantize(W0, H, bits=4, replay=rep)
-        assert rep.hard == 1
+
+
+def _adjudicate_codes(t, theirs, zero, maxq=15, band=1e-3):
+    """One column through TieReplay.code with hand-made pre-rounding values t."""
+    t = np.asarray(t, np.float32)
+    theirs = np.asarray(theirs, np.int64)
+    n = t.size
+    zero = np.broadcast_to(np.asarray(zero, np.float64), (n,)).copy()
+    rep = ref.TieReplay(theirs.reshape(n, 1), band=band)
+    mine = np.clip(np.rint(t.astype(np.float64)) + zero, 0, maxq)
+    out = rep.code(np.arange(n), 0, mine, t, zero, maxq)
+    return mine, out, rep
+
+
+def test_tie_replay_adopts_the_other_neighbour_at_a_near_tie():
+    # zero 3; t = 4.5 +- 4e-4 and 6.5 + 9e-4 (inside the band of 1e-3).
+    t = [4.5 + 4e-4, 4.5 - 4e-4, 6.5 + 9e-4]
+    mine, _, _ = _adjudicate_codes(t, [0, 0, 0], 3)
+    np.testing.assert_array_equal(mine, [8, 7, 10])          # the oracle's own picks
+    theirs = [7, 8, 9]                                       # the other neighbour each time
+    _, out, rep = _adjudicate_codes(t, theirs, 3)
+    np.testing.assert_array_equal(out, theirs)
+    assert rep.near_ties == 3 and rep.hard == 0
+
+
+def test_tie_replay_rejects_a_neighbour_away_from_a_midpoint():
+    # A neighbouring tick is not a valid choice when t is far from a midpoint,
+    # nor just outside the band (1.5e-3 and 2e-3 away).
+    t = [4.3, 4.7, 4.5 + 2e-3, 4.5 - 1.5e-3]
+    mine, _, _ = _adjudicate_codes(t, [0, 0, 0, 0], 3)
+    np.testing.assert_array_equal(mine, [7, 8, 8, 7])
+    _, out, rep = _adjudicate_codes(t, [8, 7, 7, 8], 3)
+    np.testing.assert_array_equal(out, mine)                  # the oracle keeps its own
+    assert rep.hard == 4 and rep.near_ties == 0
+
+
+def test_tie_replay_rejects_a_non_neighbour_at_a_near_tie():
+    # t = 4.5 exactly: the neighbours are 4 and 5 (codes 7 and 8 with zero 3);
+    # codes two ticks away are never valid.
+    t = [4.5, 4.5, 4.5 + 1e-4, 4.5 - 1e-4]
+    mine, _, _ = _adjudicate_codes(t, [0] * 4, 3)
+    _, out, rep = _adjudicate_codes(t, [9, 6, 10, 5], 3)
+    np.testing.assert_array_equal(out, mine)
+    assert rep.hard == 4 and rep.near_ties == 0
+
+
+def test_tie_replay_neighbours_are_clamped_to_the_grid():
+    # zero 8, 4 bits: t = 7.5 sits between ticks 15 and 16, and 16 clamps to
+    # 15, so only 15 is valid; at the bottom t = -8.5 gives -1 and 0 -> 0.
+    t = [7.5 + 1e-4, -8.5 + 1e-4, 6.5 + 1e-4]
+    mine, _, _ = _adjudicate_codes(t, [0] * 3, 8)
+    np.testing.assert_array_equal(mine, [15, 0, 15])
+    _, out, rep = _adjudicate_codes(t, [14, 1, 14], 8)
+    # 14 is a neighbour of 6.5 (ticks 14 and 15) but not of 7.5; 1 is not a
+    # neighbour of -8.5 once clamped.
+    np.testing.assert_array_equal(out, [15, 0, 14])
+    assert rep.near_ties == 1 and rep.hard == 2
+
+
+def _adjudicate_zero(zt, theirs, band=1e-3):
+    zt = np.asarray(zt, np.float32)
+    n = zt.size
+    rep = ref.TieReplay(np.zeros((n, 1), np.int64), zeros=np.asarray(theirs).reshape(n, 1), band=band)
+    mine = np.rint(zt.astype(np.float64))
+    return mine, rep.zero(np.arange(n), 0, mine, zt), rep
+
+
+def test_tie_replay_zero_point_branch():
+    # Adopted: -min/scale within the band of a half-integer, other neighbour.
+    zt = [9.5 + 3e-4, 9.5 - 3e-4]
+    mine, out, rep = _adjudicate_zero(zt, [9, 10])
+    np.testing.assert_array_equal(mine, [10, 9])
+    np.testing.assert_array_equal(out, [9, 10])
+    assert rep.zero_near_ties == 2 and rep.zero_hard == 0
+    # Hard: a neighbour far from the midpoint, outside the band, and a
+    # non-neighbour at the midpoint.
+    zt = [9.2, 9.5 + 2e-3, 9.5 + 1e-4, 9.5 - 1e-4]
+    mine, out, rep = _adjudicate_zero(zt, [10, 9, 11, 8])
+    np.testing.assert_array_equal(out, mine)
+    assert rep.zero_hard == 4 and rep.zero_near_ties == 0
+    # The code counters are untouched by the zero branch, and no zeros given
+    # means nothing to adjudicate.
+    assert rep.hard == 0 and rep.near_ties == 0
+    none = ref.TieReplay(np.zeros((1, 1), np.int64))
+    assert none.zero(np.arange(1), 0, np.array([4.0]), np.array([4.5], np.float32))[0] == 4.0
+
+
+def test_tie_replay_adopted_code_flows_into_the_outputs():
+    # H = 8 I: no repairs, so each pre-rounding value is the weight itself.
+    # Row 0's column 5 is placed 2e-4 above a midpoint; an implementation
+    # that picked the lower neighbour is adopted there and nowhere else.
+    rng = np.random.default_rng(23)
+    r, c = 3, 16
+    W0 = rng.uniform(-0.7, 0.3, size=(r, c))
+    W0[:, 0], W0[:, 1] = -0.8, 0.4                            # rulers: scale 0.08, zero 10
+    scale = np.float32(0.8 + 0.4) / np.float32(15)
+    W0[0, 5] = float(np.float32((2.5 + 2e-4) * float(scale)))
+    H = 8.0 * np.eye(c)
+    base = ref.gptq_quantize(W0, H, bits=4, percdamp=0.0)
+    assert base["codes"][0, 5] == 13
+    theirs = base["codes_proc"].copy()
+    theirs[0, 5] = 12
+    rep = ref.TieReplay(theirs, base["zeros"])
+    out = ref.gptq_quantize(W0, H, bits=4, percdamp=0.0, replay=rep)
+    assert rep.near_ties == 1 and rep.hard == 0
+    np.testing.assert_array_equal(out["codes"], theirs)
+    assert out["w_hat"][0, 5] == pytest.approx(float(scale) * 2, rel=1e-7)
 
 
 # --- P14: packed layout (this project's layout; the pages fix none) ---
