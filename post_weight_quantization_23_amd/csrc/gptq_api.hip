@@ -34,6 +34,11 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr int64_t kMaxDim = 65535;       // H / U edge (grid y limit, int kernels)
 constexpr int64_t kMaxRows = INT_MAX / 2; // rows of W, tokens of X
+// A launch's grid.x times its 256 threads per workgroup must fit in 32 bits.
+constexpr int64_t kMaxGroups256 = ((int64_t(1) << 32) - 1) / 256;
+
+// Workgroups of 256 threads needed for n items at `per` items per workgroup.
+int64_t groups_for(int64_t n, int64_t per) { return (n + per - 1) / per; }
 
 size_t elem_size(gptq_dtype t) { return t == GPTQ_F32 ? 4 : 2; }
 bool valid_dtype(int t) { return t == GPTQ_F32 || t == GPTQ_BF16 || t == GPTQ_F16; }
@@ -90,7 +95,7 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t d, const void* X, gptq_dty
   if (xt != GPTQ_F32) need = gptq::syrk_workspace_bytes(gptq::plan_syrk(d, n_tok));
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(GPTQ_EWORKSPACE, fn, "workspace needs " + std::to_string(need) + " bytes");
-  if (need > 0 && !aligned(ws, 16)) return fail(GPTQ_EALIGN, fn, "workspace not 16-byte aligned");
+  if (need > 0 && !aligned(ws, 256)) return fail(GPTQ_EALIGN, fn, "workspace not 256-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (xt == GPTQ_F32) {
     gptq::GemmArgs g;
@@ -163,6 +168,7 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype wt, int64_t r, int64_t
   if (groupsize > 0 && (groupsize % blocksize) != 0 && (blocksize % groupsize) != 0)
     return fail(GPTQ_EUNSUPPORTED, fn, "groupsize must be a multiple or a divisor of blocksize");
   if (r > kMaxRows || c > kMaxDim) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (r > kMaxGroups256) return fail(GPTQ_EUNSUPPORTED, fn, "r too large: one 256-thread workgroup per row");
   if (r == 0 || c == 0) return ok();
   if (ldw < c) return fail(GPTQ_ESHAPE, fn, "ldw < c");
   if (!W || !U || !codes || !scales || !zeros || !g_idx) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
@@ -191,6 +197,9 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, cons
   if (bits == 3 && c % 32 != 0) return fail(GPTQ_ESHAPE, fn, "3-bit packing needs c % 32 == 0");
   if (ld_words < c * bits / 32) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
   if (r > kMaxRows || c > (int64_t)INT_MAX) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  // one thread per packed chunk (8 codes at 4 bits, 32 codes at 3 bits or with col_perm)
+  if (groups_for(r * groups_for(c, (bits == 4 && !col_perm) ? 8 : 32), 256) > kMaxGroups256)
+    return fail(GPTQ_EUNSUPPORTED, fn, "too many packed chunks for one launch");
   if (r == 0 || c == 0) return ok();
   if (!codes || !packed) return fail(GPTQ_EINVAL, fn, "codes or packed is NULL");
   if (!aligned(codes, 16) || !aligned(packed, 4)) return fail(GPTQ_EALIGN, fn, "codes must be 16-byte aligned");
@@ -248,6 +257,9 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
   if (rows == 0 || d == 0) return ok();
   if (lda < d || ldo < d) return fail(GPTQ_ESHAPE, fn, "lda and ldo must be >= d");
   if ((rows * (d / block)) >= (int64_t)INT_MAX) return fail(GPTQ_EUNSUPPORTED, fn, "too many blocks");
+  // one workgroup per tile of 4096 elements (8192 for b = 8192)
+  if (groups_for(rows * (d / block), block == 8192 ? 1 : 4096 / block) > kMaxGroups256)
+    return fail(GPTQ_EUNSUPPORTED, fn, "too many tiles for one launch");
   if (!A || !out) return fail(GPTQ_EINVAL, fn, "A or out is NULL");
   if (!aligned(A, elem_size(at)) || !aligned(out, elem_size(ot))) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
   const char* a0 = static_cast<const char*>(A);
@@ -274,7 +286,7 @@ gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int
   if (act != 0 && act != 1) return fail(GPTQ_EINVAL, fn, "act must be 0 (none) or 1 (silu(G) * up)");
   if (d < 64 || d % 64 != 0) return fail(GPTQ_EUNSUPPORTED, fn, "d must be a positive multiple of 64");
   if (r > (int64_t)INT_MAX / 2 || d > (int64_t)INT_MAX / 2 || n_tok > kMaxRows ||
-      ((n_tok + 255) / 256) * ((r + 255) / 256) >= (int64_t)INT_MAX)   // one workgroup per 256 x 256 tile
+      groups_for(n_tok, 256) * groups_for(r, 256) > kMaxGroups256)   // one workgroup per 256 x 256 tile
     return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
   if (n_tok == 0 || r == 0) return ok();
   if (ldx < d || ldw < d || ldy < r || (act == 1 && ldg < r)) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");
@@ -309,7 +321,7 @@ gptq_status gptq_round16(const float* src, int64_t rows, int64_t cols, int64_t l
   if (rows < 0 || cols < 0) return fail(GPTQ_EINVAL, fn, "negative size");
   if (!valid_dtype(dt)) return fail(GPTQ_EINVAL, fn, "dt must be a gptq_dtype value");
   if (dt == GPTQ_F32) return fail(GPTQ_EDTYPE, fn, "dt must be GPTQ_BF16 or GPTQ_F16");
-  if (rows > kMaxRows || cols > kMaxRows || rows * ((cols + 3) / 4) / 256 >= (int64_t)INT_MAX)
+  if (rows > kMaxRows || cols > kMaxRows || groups_for(rows * ((cols + 3) / 4), 256) > kMaxGroups256)
     return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
   if (rows == 0 || cols == 0) return ok();
   if (lds < cols || ldd < cols) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");

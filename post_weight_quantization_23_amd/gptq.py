@@ -34,15 +34,21 @@ def _stream():
     return C.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _need(t, name, dtype=None, ndim=None, dev=None):
+def _need(t, name, dtype=None, ndim=None, dev=None, on_gpu=True):
+    """Type, dtype and rank of one argument; then (on_gpu) its device."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must be {ndim}-D")
+    if on_gpu:
+        _on_gpu(t, name, dev)
+
+
+def _on_gpu(t, name, dev=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
     if dev is not None and t.device != dev:
         raise ValueError(f"{name} is on {t.device}, expected {dev}")
 
@@ -122,22 +128,42 @@ def quantize_layer(W: torch.Tensor, U: torch.Tensor, perm: torch.Tensor | None, 
     original column order.  `out` may supply preallocated tensors with those keys.
     `sym` selects the symmetric ruler (zero point at the middle tick).
     """
-    _need(W, "W", None, 2)
+    # Every shape, dtype and layout is checked before the devices, and all of
+    # it before anything is allocated: the kernels index perm, dead and the
+    # outputs by r and c, so a short or mis-shaped tensor must not get through.
+    _need(W, "W", None, 2, on_gpu=False)
     if W.dtype not in _DT:
         raise TypeError("W must be float32, bfloat16 or float16")
     if W.stride(1) != 1:
         raise ValueError("W must have unit column stride")
     r, c = W.shape
-    _need(U, "U", torch.float32, 2, W.device)
+    _need(U, "U", torch.float32, 2, on_gpu=False)
     if U.shape != (c, c) or not U.is_contiguous():
         raise ValueError("U must be a contiguous [c, c] matrix")
-    if perm is not None:
-        _need(perm, "perm", torch.int32, 1, W.device)
-    if dead is not None:
-        _need(dead, "dead", torch.uint8, 1, W.device)
+    for v, name, dt in ((perm, "perm", torch.int32), (dead, "dead", torch.uint8)):
+        if v is not None:
+            _need(v, name, dt, 1, on_gpu=False)
+            if v.numel() != c or not v.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous vector of length c = {c}")
     G = (c + groupsize - 1) // groupsize if groupsize > 0 else 1
-    dev = W.device
     o = dict(out or {})
+    unknown = set(o) - {"codes", "scales", "zeros", "g_idx", "w_hat", "row_loss"}
+    if unknown:
+        raise ValueError(f"unknown output names {sorted(unknown)}")
+    shapes = {"codes": ((r, c), torch.uint8), "scales": ((r, G), torch.float32), "zeros": ((r, G), torch.int32),
+              "g_idx": ((c,), torch.int32), "w_hat": ((r, c), torch.float32), "row_loss": ((r,), torch.float32)}
+    for k, t in o.items():
+        if t is None:
+            continue
+        shape, dt = shapes[k]
+        _need(t, f"out[{k!r}]", dt, len(shape), on_gpu=False)
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"out[{k!r}] must be a contiguous {dt} tensor of shape {shape}")
+    _on_gpu(W, "W")
+    dev = W.device
+    for t, name in ((U, "U"), (perm, "perm"), (dead, "dead"), *((t, f"out[{k!r}]") for k, t in o.items())):
+        if t is not None:
+            _on_gpu(t, name, dev)
     codes = o.get("codes") if o.get("codes") is not None else torch.empty((r, c), dtype=torch.uint8, device=dev)
     scales = o.get("scales") if o.get("scales") is not None else torch.empty((r, G), dtype=torch.float32, device=dev)
     zeros = o.get("zeros") if o.get("zeros") is not None else torch.empty((r, G), dtype=torch.int32, device=dev)

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_symbols_are_exported(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -222,3 +222,79 @@ def test_python_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         gptq.dequant_gemv(torch.zeros(2, 4, dtype=torch.uint32), torch.zeros(2, 1), torch.zeros(2, 1, dtype=torch.int32),
                           torch.zeros(32, dtype=torch.bfloat16), 4, -1)
+
+
+def test_python_quantize_layer_checks_lengths_and_outputs_before_the_device():
+    # The kernels index perm / dead by column and write every output with
+    # strides r and c, so the binding rejects a short or mis-shaped tensor
+    # (these are CPU tensors: the shape checks come before the device check).
+    import torch
+    from post_weight_quantization_23_amd import gptq
+    r, c = 4, 64
+    W = torch.zeros(r, c)
+    U = torch.zeros(c, c)
+    ok_perm = torch.zeros(c, dtype=torch.int32)
+    ok_dead = torch.zeros(c, dtype=torch.uint8)
+
+    def q(**kw):
+        args = dict(W=W, U=U, perm=ok_perm, dead=ok_dead)
+        args.update(kw)
+        return gptq.quantize_layer(args.pop("W"), args.pop("U"), args.pop("perm"), args.pop("dead"), **args)
+
+    with pytest.raises(ValueError, match="perm"):
+        q(perm=torch.zeros(c - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="dead"):
+        q(dead=torch.zeros(c + 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="perm"):
+        q(perm=torch.zeros(2 * c, dtype=torch.int32)[::2])
+    with pytest.raises(TypeError, match="perm"):
+        q(perm=torch.zeros(c, dtype=torch.int64))
+    with pytest.raises(ValueError, match="U"):
+        q(U=torch.zeros(c, c + 1))
+    bad_outs = {
+        "codes": torch.zeros(r, c - 1, dtype=torch.uint8),
+        "scales": torch.zeros(r, 2),                 # groupsize 128 > c: one group
+        "zeros": torch.zeros(r + 1, 1, dtype=torch.int32),
+        "g_idx": torch.zeros(c + 8, dtype=torch.int32),
+        "w_hat": torch.zeros(c, r),
+        "row_loss": torch.zeros(2 * r)[::2],
+    }
+    for k, t in bad_outs.items():
+        with pytest.raises(ValueError, match=k):
+            q(out={k: t})
+    with pytest.raises(TypeError, match="codes"):
+        q(out={"codes": torch.zeros(r, c, dtype=torch.int32)})
+    with pytest.raises(ValueError, match="unknown"):
+        q(out={"code": torch.zeros(r, c, dtype=torch.uint8)})
+    # Everything well formed: only then does the device check fire.
+    with pytest.raises(ValueError, match="GPU"):
+        q(out={"codes": torch.zeros(r, c, dtype=torch.uint8)})
+
+
+def test_launch_grids_are_bounded_at_the_exact_limit(lib):
+    # A launch's grid.x * 256 threads must fit in 32 bits: at most 2^24 - 1
+    # workgroups.  Each size is tried one past the limit (rejected as
+    # unsupported) and at the limit (accepted by the size check, then stopped
+    # by a NULL pointer or a missing workspace, so nothing is launched).
+    A = ALIGNED
+    lim = (1 << 24) - 1
+    q = lambda r, ws: _st(lib, "gptq_quantize_layer", A, 1, r, 256, 256, A, None, None, 4, 0, 128, 128, A, A, A, A,
+                          None, None, ws, 1 << 40 if ws else 0, None)
+    assert q(lim + 1, A) == 5 and q(lim, None) == 6                    # one workgroup per row
+    l = lambda x, r: _st(lib, "gptq_linear_forward", x, 1, 1 << 20, 256, 256, C.c_void_p(0x1000000), 0, r, 256,
+                         0, None, 0, C.c_void_p(0x40000000), 1, r, None)
+    assert l(A, 1 << 20) == 5 and l(None, (1 << 20) - 256) == 1        # 2^12 x 2^12 tiles vs 2^12 x (2^12 - 1)
+    rr = lambda s, rows: _st(lib, "gptq_round16", s, rows, 1024, 1024, 1, C.c_void_p(0x40000000), 1024, None)
+    assert rr(A, lim + 1) == 5 and rr(None, lim) == 1                  # 256 four-element items per row
+    p = lambda c, r, perm: _st(lib, "gptq_pack", c, r, 2048, 4, perm, A, 256, None)
+    assert p(A, lim + 1, None) == 5 and p(None, lim, None) == 1        # 256 chunks of 8 codes per row
+    assert p(A, 4 * (lim + 1), A) == 5 and p(None, 4 * lim, A) == 1    # 64 chunks of 32 codes per row
+    h = lambda a, rows: _st(lib, "gptq_hadamard_rotate", a, 1, rows, 4096, 4096, 4096, C.c_void_p(0x40000000), 1,
+                            4096, None)
+    assert h(A, lim + 1) == 5 and h(None, lim) == 1                    # one tile of 4096 per workgroup
+
+
+def test_hessian_workspace_must_be_256_byte_aligned(lib):
+    f = "gptq_hessian_accumulate"
+    base = lambda ws: _st(lib, f, ALIGNED, 4096, ALIGNED, 1, 262144, 4096, ws, 1 << 40, None)
+    assert base(C.c_void_p(0x10010)) == 4 and base(C.c_void_p(0x10080)) == 4
