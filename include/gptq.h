@@ -253,8 +253,8 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
 /* ------------------------------------------------------------------------
  * Forward pass of a quantized linear layer over calibration tokens, for the
  * layer-by-layer pass.  Page: "What is GPTQ" (queryfeedz glossary), section
- * "How it works": each layer is quantized in turn and the next layer is
- * calibrated on the quantized outputs of the previous one.
+ * "How it works": layers are quantized in sequence, and each one is
+ * calibrated on what the already-quantized layers before it produce.
  *
  *   act == 0:  Y[t, i] = round_yt( sum_k X[t, k] * round_xt(W_hat[i, k]) )
  *   act == 1:  Y[t, i] = round_yt( silu(G[t, i]) * round_xt(sum_k ...) ),
@@ -299,6 +299,12 @@ gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int
  * ------------------------------------------------------------------------ */
 gptq_status gptq_round16(const float* src, int64_t rows, int64_t cols, int64_t lds,
                          gptq_dtype dt, void* dst, int64_t ldd, void* stream);
+
+/* SHA-256 (hex, static storage) of the sources this library was built from:
+ * every file under csrc/ and this header, as the in-tree build hashes them.
+ * The Python loader refuses a library whose id differs from the sources
+ * beside it, so a stale build is never run. */
+const char* gptq_build_id(void);
 
 /* Human-readable name of a status code (static storage). */
 const char* gptq_status_string(gptq_status s);

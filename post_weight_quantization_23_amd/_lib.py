@@ -34,6 +34,7 @@ SIGNATURES = {
     "gptq_linear_forward": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _P, C.c_int, _I64, _I64, C.c_int, _P, _I64,
                                       _P, C.c_int, _I64, _P]),
     "gptq_round16": (C.c_int, [_P, _I64, _I64, _I64, C.c_int, _P, _I64, _P]),
+    "gptq_build_id": (C.c_char_p, []),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_last_error": (C.c_char_p, []),
 }
@@ -48,7 +49,8 @@ class GPTQError(RuntimeError):
 
 
 def load() -> C.CDLL:
-    """Load the HIP library once; raise if it is not built."""
+    """Load the HIP library once; raise if it is not built or was built from
+    other sources than the ones beside it."""
     global _lib
     if _lib is not None:
         return _lib
@@ -59,6 +61,11 @@ def load() -> C.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    from .build import source_id
+    built, here = lib.gptq_build_id().decode(), source_id()
+    if built != here:
+        raise RuntimeError(f"{LIB_PATH} is stale: built from sources {built[:12]}, the sources here are "
+                           f"{here[:12]}; rebuild with `python -m post_weight_quantization_23_amd.build`")
     _lib = lib
     return lib
 
