@@ -578,8 +578,8 @@ def hadamard_rotate(A, block: int | None = None) -> np.ndarray:
 
 # ---------------------------------------------------------------------------
 # Layer by layer -- "What is GPTQ" (queryfeedz glossary), section "How it
-# works": layers are quantized one at a time and each next layer is
-# calibrated on the quantized outputs of the previous one; "Post-Training
+# works": layers are quantized in sequence, each calibrated on what the
+# already-quantized layers before it produce; "Post-Training
 # Quantization: Calibration, GPTQ and Why Rotations Help", section
 # "Calibration: letting data pick the rounding": the layer's calibration
 # inputs are what the (already quantized) model feeds it.

@@ -533,22 +533,24 @@ void launch_tile(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
   if (t0 + t1 == 0) return;
   if (dma_ok(g0) && (!g1 || dma_ok(*g1))) {
     constexpr size_t smem = (size_t)2 * KT * (TM + TN) * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
+    // set once per instantiation; a function-local static is initialised
+    // exactly once even when several host threads launch concurrently
+    static const bool attr = [&] {
       (void)hipFuncSetAttribute((const void*)gemm_f32_dma_kernel<TM, TN, KT>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-      attr = true;
-    }
+      return true;
+    }();
+    (void)attr;
     hipLaunchKernelGGL((gemm_f32_dma_kernel<TM, TN, KT>), dim3((unsigned)(t0 + t1)), dim3(256), smem, s, pr);
     return;
   }
   constexpr size_t smem = (size_t)2 * KT * ((TM + PAD) + (TN + PAD)) * sizeof(float);
-  static bool attr = false;
-  if (!attr) {
+  static const bool attr = [&] {   // once, thread-safe (function-local static)
     (void)hipFuncSetAttribute((const void*)gemm_f32_kernel<TM, TN, KT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)smem);
-    attr = true;
-  }
+    return true;
+  }();
+  (void)attr;
   hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, KT>), dim3((unsigned)(t0 + t1)), dim3(256), smem, s, pr);
 }
 

@@ -1,8 +1,8 @@
 // Forward pass of a quantized linear layer over the calibration tokens:
 //     Y[t, i] = act( sum_k X[t, k] * round16(W_hat[i, k]) )
 // The page "What is GPTQ" (queryfeedz glossary), section "How it works":
-// layers are processed one at a time and the next layer is calibrated on the
-// quantized outputs of the previous one.  This kernel produces those outputs:
+// layers are processed in sequence, each calibrated on what the already-
+// quantized layers before it produce.  This kernel produces those inputs:
 // the dequantized weights W_hat (fp32, as the quantizer writes them) are
 // rounded once to the activations' 16-bit type (the model's own precision),
 // products are exact in fp32 and sums are fp32 (MFMA), and the result is
@@ -496,12 +496,12 @@ void launch_linear(const void* X, int xt, int64_t n_tok, int64_t d, int64_t ldx,
   // 128 KiB of dynamic LDS: A and B, double buffered
 #define GPTQ_LIN(D_, A_, Y_, W_)                                                                      \
   do {                                                                                                \
-    static bool set = false;                                                                          \
-    if (!set) {                                                                                       \
+    static const bool set = [&] { /* once, thread-safe (function-local static) */                     \
       (void)hipFuncSetAttribute((const void*)linear_kernel<D_, A_, Y_, W_>,                           \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                \
-      set = true;                                                                                     \
-    }                                                                                                 \
+      return true;                                                                                    \
+    }();                                                                                              \
+    (void)set;                                                                                        \
     hipLaunchKernelGGL((linear_kernel<D_, A_, Y_, W_>), grid, dim3(256), lds, s, a);                 \
   } while (0)
 #define GPTQ_LIN_W(D_, A_, Y_)                  \

@@ -349,12 +349,12 @@ size_t prepare_workspace_bytes(int64_t d, int act_order) {
 
 void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t* perm, uint8_t* dead,
                     int32_t* info, void* ws, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static const bool attr_set = [] {   // once, thread-safe (function-local static)
     (void)hipFuncSetAttribute((const void*)leaf_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)leaf_smem_bytes());
-    attr_set = true;
-  }
+                              (int)leaf_smem_bytes());
+    return true;
+  }();
+  (void)attr_set;
   const size_t mat = (size_t)d * (size_t)d * sizeof(float);
   float* Wk = reinterpret_cast<float*>(ws);
   float* diag = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((mat + 255) / 256) * 256);

@@ -473,14 +473,14 @@ void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok,
                    const SyrkPlan& p, float* ws, hipStream_t s) {
   const int nt = (int)((d + TILE - 1) / TILE);
   const size_t shmem = 4 * TILE * ROWB;  // 128 KiB: A and B, double buffered
-  static bool attr_set = false;
-  if (!attr_set) {
+  static const bool attr_set = [&] {   // once, thread-safe (function-local static)
     (void)hipFuncSetAttribute((const void*)syrk16_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     (void)hipFuncSetAttribute((const void*)syrk16_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    attr_set = true;
-  }
+    return true;
+  }();
+  (void)attr_set;
   dim3 grid((unsigned)(p.tiles * p.splits));
   float* part = p.splits > 1 ? ws : nullptr;
   const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0) && ldx < (int64_t(1) << 24);

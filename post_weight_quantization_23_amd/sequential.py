@@ -1,8 +1,8 @@
 """Layer-by-layer GPTQ over a stack of gated MLP blocks, every step a HIP kernel.
 
 The pages: "What is GPTQ" (queryfeedz glossary), section "How it works" --
-layers are quantized one at a time and each next layer is calibrated on the
-quantized outputs of the previous one; "Post-Training Quantization:
+layers are quantized in sequence, and the calibration inputs of each one
+are what the already-quantized layers before it produce; "Post-Training Quantization:
 Calibration, GPTQ and Why Rotations Help", section "Calibration: letting data
 pick the rounding" -- one layer at a time keeps memory small.
 
