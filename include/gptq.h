@@ -116,6 +116,27 @@ gptq_status gptq_prepare(float* H_to_U, int64_t d, float percdamp, int act_order
                          size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gptq_prepare without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same operation, arguments, kernels and
+ * results (bit for bit) as gptq_prepare; the scratch it needs lives in a
+ * static device array of the library, GPTQ_PREPARE_NOALLOC_SCRATCH_BYTES
+ * bytes on each GPU the library runs on, held until the process ends.
+ *
+ * d      : 1 .. GPTQ_PREPARE_NOALLOC_MAX_D (4096); larger d returns
+ *          GPTQ_EUNSUPPORTED (use gptq_prepare with a workspace).
+ * The call allocates nothing (no hipMalloc, no library allocation).  Every
+ * call on one GPU uses that GPU's one scratch array: calls that overlap in
+ * time on one GPU (two streams, two host threads) race and must be ordered
+ * by the caller.  The first call on each device looks up the array's device
+ * address (hipGetSymbolAddress); GPTQ_EHIP if that fails.
+ * ------------------------------------------------------------------------ */
+#define GPTQ_PREPARE_NOALLOC_MAX_D 4096
+#define GPTQ_PREPARE_NOALLOC_SCRATCH_BYTES (4096ull * 4096ull * 4ull + 4096ull * 4ull + 256ull)
+gptq_status gptq_prepare_noalloc(float* H_to_U, int64_t d, float percdamp, int act_order,
+                                 int32_t* perm, uint8_t* dead, int32_t* info, void* stream);
+
+/* ------------------------------------------------------------------------
  * Quantize one layer.  Page: "GPTQ, with the code open", sections "What
  * quantization is" (ruler), "The repair rule" and "From one repair to a whole
  * model" (the column loop, the per-weight loss (w - q)^2 / (2 d^2), blocks of

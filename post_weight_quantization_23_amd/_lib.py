@@ -25,6 +25,7 @@ SIGNATURES = {
     "gptq_hessian_accumulate": (C.c_int, [_P, _I64, _P, C.c_int, _I64, _I64, _P, _SZ, _P]),
     "gptq_prepare_workspace_size": (C.c_int, [_I64, C.c_int, _SZP]),
     "gptq_prepare": (C.c_int, [_P, _I64, C.c_float, C.c_int, _P, _P, _P, _P, _SZ, _P]),
+    "gptq_prepare_noalloc": (C.c_int, [_P, _I64, C.c_float, C.c_int, _P, _P, _P, _P]),
     "gptq_quantize_layer_workspace_size": (C.c_int, [_I64, _I64, _I64, _SZP]),
     "gptq_quantize_layer": (C.c_int, [_P, C.c_int, _I64, _I64, _I64, _P, _P, _P, C.c_int, C.c_int, _I64, _I64,
                                       _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -5,6 +5,7 @@
 // allocates nothing; scratch space is the caller's workspace.
 #include <climits>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/gptq.h"
@@ -42,6 +43,35 @@ int64_t groups_for(int64_t n, int64_t per) { return (n + per - 1) / per; }
 
 size_t elem_size(gptq_dtype t) { return t == GPTQ_F32 ? 4 : 2; }
 bool valid_dtype(int t) { return t == GPTQ_F32 || t == GPTQ_BF16 || t == GPTQ_F16; }
+
+// Scratch of gptq_prepare_noalloc: one array per GPU, as large as
+// gptq_prepare's workspace at the largest supported d.  In host code the
+// name `scratch` is only a stand-in; its device address on the current
+// device comes from hipGetSymbolAddress (looked up once per device and kept).
+static __device__ __align__(256) unsigned char scratch[GPTQ_PREPARE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
@@ -139,6 +169,32 @@ gptq_status gptq_prepare(float* H, int64_t d, float percdamp, int act_order, int
   const size_t need = gptq::prepare_workspace_bytes(d, act_order);
   if (!ws || ws_bytes < need) return fail(GPTQ_EWORKSPACE, fn, "workspace needs " + std::to_string(need) + " bytes");
   if (!aligned(ws, 256)) return fail(GPTQ_EALIGN, fn, "workspace not 256-byte aligned");
+  gptq::launch_prepare(H, d, percdamp, act_order, perm, dead, info, ws, reinterpret_cast<hipStream_t>(stream));
+  return check_launch(fn);
+}
+
+gptq_status gptq_prepare_noalloc(float* H, int64_t d, float percdamp, int act_order, int32_t* perm,
+                                 uint8_t* dead, int32_t* info, void* stream) {
+  const char* fn = "gptq_prepare_noalloc";
+  if (d < 0) return fail(GPTQ_EINVAL, fn, "negative size");
+  if (act_order != 0 && act_order != 1) return fail(GPTQ_EINVAL, fn, "act_order must be 0 or 1");
+  if (!(percdamp >= 0.f) || !(percdamp < 1e30f)) return fail(GPTQ_EINVAL, fn, "percdamp must be finite and >= 0");
+  if (d > GPTQ_PREPARE_NOALLOC_MAX_D)
+    return fail(GPTQ_EUNSUPPORTED, fn, "d > " + std::to_string(GPTQ_PREPARE_NOALLOC_MAX_D) +
+                                           ": the static scratch is too small; use gptq_prepare with a workspace");
+  if (!info) return fail(GPTQ_EINVAL, fn, "info is NULL");
+  if (d == 0) return fail(GPTQ_EINVAL, fn, "d == 0 (nothing to factor)");
+  if (!H) return fail(GPTQ_EINVAL, fn, "H is NULL");
+  if (!dead) return fail(GPTQ_EINVAL, fn, "dead is NULL");
+  if (act_order && !perm) return fail(GPTQ_EINVAL, fn, "perm is NULL with act_order");
+  if (!aligned(H, 16) || !aligned(info, 4) || (perm && !aligned(perm, 4)))
+    return fail(GPTQ_EALIGN, fn, "H must be 16-byte aligned, perm and info 4-byte aligned");
+  static_assert(GPTQ_PREPARE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+  if (gptq::prepare_workspace_bytes(d, act_order) > GPTQ_PREPARE_NOALLOC_SCRATCH_BYTES)
+    return fail(GPTQ_EUNSUPPORTED, fn, "workspace exceeds the static scratch");
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return fail(GPTQ_EHIP, fn, std::string("scratch lookup: ") + hipGetErrorString(e));
   gptq::launch_prepare(H, d, percdamp, act_order, perm, dead, info, ws, reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);
 }

@@ -15,7 +15,7 @@ import torch
 from . import _lib
 from ._lib import GPTQ_BF16, GPTQ_F16, GPTQ_F32, GPTQError
 
-__all__ = ["hessian_accumulate", "prepare", "quantize_layer", "pack", "dequant_gemv", "hadamard_rotate",
+__all__ = ["hessian_accumulate", "prepare", "prepare_noalloc", "quantize_layer", "pack", "dequant_gemv", "hadamard_rotate",
            "linear_forward", "Workspace",
            "NotPositiveDefinite", "GPTQError"]
 
@@ -114,6 +114,38 @@ def prepare(H: torch.Tensor, percdamp: float = 0.01, act_order: bool = False, ch
         v = int(info.item())
         if v != 0:
             raise NotPositiveDefinite(f"gptq_prepare info = {v}")
+    return perm, dead, info
+
+
+def prepare_noalloc(H: torch.Tensor, percdamp: float = 0.01, act_order: bool = False,
+                    perm: torch.Tensor | None = None, dead: torch.Tensor | None = None,
+                    info: torch.Tensor | None = None):
+    """prepare() through the allocation-free entry point (d <= 4096): the
+    library's static scratch replaces the workspace.  perm / dead / info may
+    be passed preallocated (int32 [d], uint8 [d], int32 [1]); nothing is
+    synchronised or checked on the device -- read info afterwards."""
+    _need(H, "H", torch.float32, 2, on_gpu=False)
+    d = H.shape[0]
+    if H.shape != (d, d) or not H.is_contiguous():
+        raise ValueError("H must be a contiguous square matrix")
+    for t, name, dt, n in ((perm, "perm", torch.int32, d), (dead, "dead", torch.uint8, d),
+                           (info, "info", torch.int32, 1)):
+        if t is not None:
+            _need(t, name, dt, 1, on_gpu=False)
+            if t.numel() != n or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous vector of length {n}")
+    _on_gpu(H, "H")
+    for t, name in ((perm, "perm"), (dead, "dead"), (info, "info")):
+        if t is not None:
+            _on_gpu(t, name, H.device)
+    if perm is None:
+        perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    if dead is None:
+        dead = torch.empty(d, dtype=torch.uint8, device=H.device)
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=H.device)
+    _lib.call("gptq_prepare_noalloc", _ptr(H), d, float(percdamp), int(act_order), _ptr(perm), _ptr(dead),
+              _ptr(info), _stream())
     return perm, dead, info
 
 

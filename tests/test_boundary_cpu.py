@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_symbols_are_exported(lib):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -298,3 +298,17 @@ def test_hessian_workspace_must_be_256_byte_aligned(lib):
     f = "gptq_hessian_accumulate"
     base = lambda ws: _st(lib, f, ALIGNED, 4096, ALIGNED, 1, 262144, 4096, ws, 1 << 40, None)
     assert base(C.c_void_p(0x10010)) == 4 and base(C.c_void_p(0x10080)) == 4
+
+
+def test_prepare_noalloc_argument_errors(lib):
+    f = "gptq_prepare_noalloc"
+    A = ALIGNED
+
+    def p(H=A, d=256, damp=0.01, ao=0, perm=None, dead=A, info=A):
+        return _st(lib, f, H, d, C.c_float(damp), ao, perm, dead, info, None)
+
+    assert p(d=-1) == 1 and p(ao=2) == 1 and p(damp=-1.0) == 1 and p(damp=float("nan")) == 1
+    assert p(d=4097) == 5                         # beyond the static scratch
+    assert p(d=0) == 1 and p(info=None) == 1 and p(H=None) == 1 and p(dead=None) == 1
+    assert p(ao=1, perm=None) == 1                # act-order needs perm
+    assert p(H=C.c_void_p(0x10004)) == 4 and p(info=C.c_void_p(0x10002)) == 4
