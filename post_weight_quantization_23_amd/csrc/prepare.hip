@@ -14,8 +14,9 @@
 //     U11 = rec(A')
 //     U12 = -U11 T U22
 // All products are fp32 matrix-core GEMMs (gemm_f32.hip).  Blocks of <= 128
-// are factored by one workgroup in LDS with the same recursion down to 32,
-// where one wave runs the column-by-column factorisation and inversion.
+// are factored by one workgroup in LDS with the same recursion down to 16,
+// where one wave runs the column-by-column factorisation and inversion (the
+// 32-level products of that wave on 16 x 16 matrix-core tiles).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -123,35 +124,36 @@ __global__ __launch_bounds__(256) void zero_lower_kernel(float* H, int64_t d) {
 // Leaf: U of one diagonal block of <= 128 in LDS.
 // ---------------------------------------------------------------------------
 
-// One wave: the 32 x 32 diagonal block of M at (o, o) holds the upper
+// One wave: the S x S diagonal block of M at (o, o) (S = 16) holds the upper
 // triangle of the (updated) H block; it is replaced by U = V^{-1} where
-// V V^T = block, V upper.  One backward sweep j = 31 .. 0 does both:
+// V V^T = block, V upper.  One backward sweep j = S-1 .. 0 does both:
 //   factor : V[:, j] = A[:, j] / sqrt(A[j][j]);  A[0:j, 0:j] -= V[0:j, j] V[0:j, j]^T
 //   invert : X[j, :] /= V[j][j];  X[0:j, :] -= V[0:j, j] X[j, :]   (X starts as I)
 // (row j of X is final at step j: every later row has already been removed).
-// Registers only: lane k < 32 holds column k of the symmetric block A, lane
-// 32 + c column c of X.  With p = A[j][j] and a_i = A[i][j] (read from lane j),
-// both updates are  col[i] -= a_i * col[j] / p  for i < j  -- on the A side
-// col[j] = A[j][k] = A[k][j] by symmetry, on the X side col[j] = X[j][c] before
-// its scaling -- and the X side then scales col[j] by 1/sqrt(p).  A non-positive
-// or NaN pivot sets *info once.
-__device__ __forceinline__ void leaf32(float* M, int o, float* /*unused*/, int32_t* info, int64_t gbase,
-                                       int pad) {
+// Registers only: lane k < S holds column k of the symmetric block A, lane
+// S + c column c of X (lanes from 2S on idle).  With p = A[j][j] and a_i =
+// A[i][j] (read from lane j), both updates are  col[i] -= a_i * col[j] / p  for
+// i < j -- on the A side col[j] = A[j][k] = A[k][j] by symmetry, on the X side
+// col[j] = X[j][c] before its scaling -- and the X side then scales col[j] by
+// 1/sqrt(p).  A non-positive or NaN pivot is recorded as the sweep goes (the
+// first one found, a wave-uniform value) and reported once at the end.
+template <int S>
+__device__ __forceinline__ void leaf_sweep(float* M, int o, int32_t* info, int64_t gbase, int pad) {
   const int lane = threadIdx.x & 63;
-  const int k = lane & 31;
-  const bool xside = lane >= 32;
-  float col[32];
+  const int k = lane % S;
+  const bool xside = lane >= S && lane < 2 * S;
+  const bool active = lane < 2 * S;
+  float col[S];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
+  for (int i = 0; i < S; ++i) {
     const float av = M[(o + min(i, k)) * LDM + o + max(i, k)];
     col[i] = xside ? (i == k ? 1.f : 0.f) : av;
   }
+  int bad = -1;   // sweep position of the first non-positive pivot found
 #pragma unroll
-  for (int j = 31; j >= 0; --j) {
+  for (int j = S - 1; j >= 0; --j) {
     const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(col[j]), j));
-    if (lane == 0 && !(piv > 0.f) && (o + j) >= pad) {
-      if (*info == 0) *info = (int32_t)(gbase + (o + j - pad) + 1);
-    }
+    bad = (bad < 0 && !(piv > 0.f)) ? j : bad;
     const float rv = __builtin_amdgcn_rsqf(piv);   // 1/sqrt(pivot), ~1 ulp
     const float f = col[j] * (rv * rv);
 #pragma unroll
@@ -163,7 +165,41 @@ __device__ __forceinline__ void leaf32(float* M, int o, float* /*unused*/, int32
   }
   if (xside) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) M[(o + i) * LDM + o + k] = (k >= i) ? col[i] : 0.f;
+    for (int i = 0; i < S; ++i) M[(o + i) * LDM + o + k] = (k >= i) ? col[i] : 0.f;
+  }
+  if (lane == 0 && bad >= 0 && (o + bad) >= pad) {
+    if (*info == 0) *info = (int32_t)(gbase + (o + bad - pad) + 1);
+  }
+  (void)active;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One wave: C (16 x 16) = alpha * A (16 x 16) * op(B) [+ C] on LDS arrays with
+// v_mfma_f32_16x16x4f32 (four steps of K = 4).  op(B) = B^T (B stored 16 x 16
+// as [n][k]) when bt, else B ([k][n]).  With upper_only only entries on and
+// above the diagonal are written.  Operand layout of the instruction: lane l
+// supplies A[l % 16][4s + l / 16] and B[4s + l / 16][l % 16]; it receives
+// D[4 (l / 16) + v][l % 16] in accumulator v.
+__device__ __forceinline__ void wave_gemm16(const float* A, int lda, const float* B, int ldb, bool bt, float* C,
+                                            int ldc, float alpha, bool accumulate, bool upper_only) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = lane >> 4;
+  floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const int kk = 4 * s4 + kq;
+    const float a = A[r * lda + kk];
+    const float b = bt ? B[r * ldb + kk] : B[kk * ldb + r];
+    d = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, d, 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int i = 4 * kq + v;
+    if (!upper_only || r >= i) {
+      float* p = C + i * ldc + r;
+      *p = accumulate ? __builtin_fmaf(alpha, d[v], *p) : alpha * d[v];
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -172,7 +208,9 @@ __device__ __forceinline__ void leaf32(float* M, int o, float* /*unused*/, int32
 // C (n x m) = alpha * A * op(B) [+ C] on LDS arrays with the fp32 matrix
 // cores; n, m, K multiples of 32.  op(B) = B^T (B stored m x K) when bt, else
 // B (K x m).  32 x 32 output blocks are spread over the 4 waves; with
-// upper_only, blocks strictly below the diagonal are skipped.
+// upper_only, blocks strictly below the diagonal are skipped.  Even and odd
+// K-pairs go to two accumulators, so consecutive MFMAs do not wait on each
+// other; the two are added at the end.
 __device__ __forceinline__ void lds_gemm(int n, int m, int K, const float* A, int lda, const float* B, int ldb, int bt,
                          float* C, int ldc, float alpha, bool accumulate, bool upper_only) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,37 +218,61 @@ __device__ __forceinline__ void lds_gemm(int n, int m, int K, const float* A, in
   for (int blk = wave; blk < blocks; blk += 4) {
     const int bi = blk / nbm, bj = blk % nbm;
     if (upper_only && bj < bi) continue;
-    floatx16 acc;
+    floatx16 acc0, acc1;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.f;
     const int r = 32 * bi + (lane & 31), c = 32 * bj + (lane & 31), kh = lane >> 5;
 #pragma unroll 8
-    for (int k = 0; k < K; k += 2) {
-      const float a = A[r * lda + k + kh];
-      const float b = bt ? B[c * ldb + k + kh] : B[(k + kh) * ldb + c];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    for (int k = 0; k < K; k += 4) {
+      const float a0 = A[r * lda + k + kh], a1 = A[r * lda + k + 2 + kh];
+      const float b0 = bt ? B[c * ldb + k + kh] : B[(k + kh) * ldb + c];
+      const float b1 = bt ? B[c * ldb + k + 2 + kh] : B[(k + 2 + kh) * ldb + c];
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc1, 0, 0, 0);
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int i = 32 * bi + 8 * (v >> 2) + 4 * kh + (v & 3);
       float* p = C + i * ldc + c;
-      *p = accumulate ? __builtin_fmaf(alpha, acc[v], *p) : alpha * acc[v];
+      const float sum = acc0[v] + acc1[v];
+      *p = accumulate ? __builtin_fmaf(alpha, sum, *p) : alpha * sum;
     }
   }
 }
 
 // In-LDS recursion on the diagonal block (o, n), n in {32, 64, 128}; level
 // temporaries T1/T2 of each size are separate (T64a/T64b for n == 128,
-// T32a/T32b for n == 64).  On return M[o:o+n, o:o+n] holds U with exact
-// zeros below the diagonal.
+// T32a/T32b for n == 64, T16a/T16b for n == 32).  On return M[o:o+n, o:o+n]
+// holds U with exact zeros below the diagonal.  With H = [[A, B], [B^T, C]]:
+//   U22 = rec(C);  T = B U22^T;  A -= T T^T;  U11 = rec(A);  U12 = -(U11 T) U22.
+// A block of 32 is done by wave 0 alone (16-wide sweeps and 16 x 16 products),
+// larger ones by all four waves.
 struct LeafScratch {
-  float *T64a, *T64b, *T32a, *T32b, *X32;
+  float *T64a, *T64b, *T32a, *T32b, *T16a, *T16b;
 };
 
 template <int N>
 __device__ __forceinline__ void leaf_rec(float* M, int o, const LeafScratch& ts, int32_t* info, int64_t gbase, int pad) {
   if constexpr (N == 32) {
-    if ((threadIdx.x >> 6) == 0) leaf32(M, o, ts.X32, info, gbase, pad);  // X32: 64-float exchange buffer
+    if ((threadIdx.x >> 6) == 0) {
+      constexpr int h = 16, ldt = 17;
+      const int o2 = o + h;
+      float* Bm = M + o * LDM + o2;
+      float* U22 = M + o2 * LDM + o2;
+      float* U11 = M + o * LDM + o;
+      leaf_sweep<16>(M, o2, info, gbase, pad);
+      wave_gemm16(Bm, LDM, U22, LDM, true, ts.T16a, ldt, 1.f, false, false);      // T = B U22^T
+      wave_gemm16(ts.T16a, ldt, ts.T16a, ldt, true, U11, LDM, -1.f, true, true);  // A -= T T^T
+      leaf_sweep<16>(M, o, info, gbase, pad);
+      wave_gemm16(U11, LDM, ts.T16a, ldt, false, ts.T16b, ldt, 1.f, false, false);  // T2 = U11 T
+      wave_gemm16(ts.T16b, ldt, U22, LDM, false, Bm, LDM, -1.f, false, false);      // U12 = -T2 U22
+      // The 32 x 32 block's lower-left quarter received the level above's
+      // update of this diagonal block (those products work on whole 32 x 32
+      // tiles); U is zero there.
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) M[(o2 + 4 * (lane >> 4) + v) * LDM + o + (lane & 15)] = 0.f;
+    }
     __syncthreads();
   } else {
     constexpr int h = N / 2;
@@ -234,7 +296,7 @@ __device__ __forceinline__ void leaf_rec(float* M, int o, const LeafScratch& ts,
   }
 }
 
-constexpr int LEAF_FLOATS = NB * LDM + 2 * 64 * 65 + 2 * 32 * 33 + 32 * 33;
+constexpr int LEAF_FLOATS = NB * LDM + 2 * 64 * 65 + 2 * 32 * 33 + 2 * 16 * 17;
 
 __global__ __launch_bounds__(256) void leaf_kernel(float* H, int64_t d, int64_t o, int n,
                                                    int32_t* info) {
@@ -245,7 +307,8 @@ __global__ __launch_bounds__(256) void leaf_kernel(float* H, int64_t d, int64_t 
   ts.T64b = ts.T64a + 64 * 65;
   ts.T32a = ts.T64b + 64 * 65;
   ts.T32b = ts.T32a + 32 * 33;
-  ts.X32 = ts.T32b + 32 * 33;
+  ts.T16a = ts.T32b + 32 * 33;
+  ts.T16b = ts.T16a + 16 * 17;
   const int pad = NB - n;
   const bool fast = pad == 0 && (d % 4) == 0 && (o % 4) == 0;
   if (fast) {
