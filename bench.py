@@ -17,6 +17,7 @@ oracle timed on a bounded sample of the same workload.
     python bench.py --gemv [--gemv-model llama7b|opt175b] [--steps K] [--warmup W]
     python bench.py --hadamard [--workload NAME] [--steps K] [--warmup W]
     python bench.py --stack [--blocks B] [--steps K] [--warmup W]
+    python bench.py --sweep [--sweep-blocks 32] [--rotate]
 
 --gemv measures the dequantizing matrix-vector product over packed layers
 instead: one step = one generated token (batch 1) through every linear layer
@@ -88,15 +89,21 @@ def copy_probe(nbytes: int = 1 << 30, reps: int = 5) -> None:
     log(f"copy probe: {reps} copies of {nbytes} bytes (read {nbytes}, write {nbytes} each)")
 
 
-def cpu_baseline(W_dev, X_dev, w, tokens_sample=16384, rows_sample=128):
-    """The oracle as it stands, on a bounded sample, extrapolated to one layer."""
+def cpu_baseline(W_dev, X_dev, w, tokens_sample=16384, rows_sample=128, cols_sample=4096):
+    """The oracle as it stands, on a bounded sample, extrapolated to one layer.
+
+    The sample: the first `cols_sample` input channels (all of them up to
+    d = 4096), `tokens_sample` tokens and `rows_sample` rows.  The oracle's H
+    costs tokens x d^2, its factor d^3 and its column loop rows x d^2, so the
+    three measured times are scaled by those ratios."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import gptq_ref as ref
 
-    X = X_dev[:tokens_sample].float().cpu().numpy()
-    W = W_dev.float().cpu().numpy()
+    dc = min(w.cols, cols_sample)
+    X = X_dev[:tokens_sample, :dc].float().cpu().numpy()
+    W = W_dev[:rows_sample, :dc].float().cpu().numpy()
     t0 = time.perf_counter()
     H = ref.hessian(X)
     t_h = time.perf_counter() - t0
@@ -104,23 +111,25 @@ def cpu_baseline(W_dev, X_dev, w, tokens_sample=16384, rows_sample=128):
     Hd, perm, dead, lam = ref.prepare(H, w.percdamp, w.act_order)
     U = ref.upper_cholesky_of_inverse(Hd)
     t_p = time.perf_counter() - t0
-    rows = np.arange(rows_sample)
     t0 = time.perf_counter()
-    ref.gptq_quantize(W[rows].astype(np.float64), H, w.bits, w.groupsize, w.percdamp, w.act_order, U=U)
+    ref.gptq_quantize(W.astype(np.float64), H, w.bits, w.groupsize, w.percdamp, w.act_order, U=U)
     t_q = time.perf_counter() - t0
-    scale_h = w.tokens / tokens_sample
-    scale_q = w.rows / rows_sample
-    sec_layer = t_h * scale_h + t_p + t_q * scale_q
+    fc = w.cols / dc
+    scale_h = (w.tokens / tokens_sample) * fc ** 2
+    scale_p = fc ** 3
+    scale_q = (w.rows / rows_sample) * fc ** 2
+    sec_layer = t_h * scale_h + t_p * scale_p + t_q * scale_q
     threads = [p.get("num_threads", 0) for p in threadpool_info()]
     cores = max(threads) if threads else 1
+    cols_note = "" if dc == w.cols else f", the first {dc} of {w.cols} input channels"
     return {
         "value": (w.rows * w.cols) / sec_layer,
         "unit": "weights/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"H on {tokens_sample} of {w.tokens} tokens (x{scale_h:g}), U on the full {w.cols}^2 H, "
-                   f"column loop on {rows_sample} of {w.rows} rows (x{scale_q:g}); linear extrapolation; "
-                   f"measured s: H {t_h:.2f}, prepare {t_p:.2f}, loop {t_q:.2f}"),
+        "sample": (f"{tokens_sample} of {w.tokens} tokens, {rows_sample} of {w.rows} rows{cols_note}; "
+                   f"H (x{scale_h:g}), factor (x{scale_p:g}), column loop (x{scale_q:g}) extrapolated by "
+                   f"tokens*d^2, d^3, rows*d^2; measured s: H {t_h:.2f}, prepare {t_p:.2f}, loop {t_q:.2f}"),
         "sec_per_layer_extrapolated": sec_layer,
         "affinity_cpus": len(os.sched_getaffinity(0)),
     }
@@ -563,6 +572,134 @@ def bench_grid(args) -> int:
     return 0
 
 
+def run_layer(q, w, W, X, ws, rotate: bool):
+    """One layer through the whole path with HIP events between the stages;
+    returns per-stage milliseconds (the rotation, when asked for, included)."""
+    import torch
+    d, r, c = w.cols, w.rows, w.cols
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    H = torch.zeros((d, d), dtype=torch.float32, device=W.device)
+    ev[0].record()
+    if rotate:
+        X = q.hadamard_rotate(X, out=X)
+        W = q.hadamard_rotate(W, out=W)
+    ev[1].record()
+    q.hessian_accumulate(H, X, ws=ws[0])
+    ev[2].record()
+    perm, dead, info = q.prepare(H, w.percdamp, w.act_order, check=False, ws=ws[1])
+    ev[3].record()
+    out = q.quantize_layer(W, H, perm, dead, bits=w.bits, groupsize=w.groupsize, blocksize=w.blocksize,
+                           ws=ws[2])
+    ev[4].record()
+    q.pack(out["codes"], w.bits)
+    ev[5].record()
+    torch.cuda.synchronize()
+    if int(info.item()) != 0:
+        raise RuntimeError(f"prepare reported info = {int(info.item())}")
+    names = ["rotate", "hessian", "prepare", "quantize", "pack"]
+    ms = {k: ev[i].elapsed_time(ev[i + 1]) for i, k in enumerate(names)}
+    ms["layer"] = ev[0].elapsed_time(ev[5])
+    return ms
+
+
+def bench_sweep(args) -> int:
+    """The 7B-shaped decoder sweep: all 224 linear layers, each with its own
+    weights and calibration activations (generated on the device before its
+    timed pass), optionally pre-rotated (rotation inside the timed pass)."""
+    import torch
+
+    from post_weight_quantization_23_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_23_amd import build as b
+        b.build()
+    import post_weight_quantization_23_amd as q
+    from synth import inputs as S
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = S.llama7b_sweep(args.sweep_blocks)
+    ws = [q.Workspace(), q.Workspace(), q.Workspace()]
+    # one untimed pass per layer shape first (first-call set-up, workspaces)
+    for w, li in {(lw.rows, lw.cols): (lw, i) for lw, i in layers}.values():
+        W, X = S.workload_device(w, layer=li, device=dev)
+        run_layer(q, w, W, X, ws, args.rotate)
+        del W, X
+    per_class, total_ms, total_w, wall_gen = {}, 0.0, 0, 0.0
+    stage_tot = {}
+    for n, (w, li) in enumerate(layers):
+        t0 = time.perf_counter()
+        W, X = S.workload_device(w, layer=li, device=dev)
+        torch.cuda.synchronize()
+        wall_gen += time.perf_counter() - t0
+        ms = run_layer(q, w, W, X, ws, args.rotate)
+        del W, X
+        key = f"{w.rows}x{w.cols}"
+        pc = per_class.setdefault(key, {"layers": 0, "ms": 0.0})
+        pc["layers"] += 1
+        pc["ms"] += ms["layer"]
+        for k, v in ms.items():
+            stage_tot[k] = stage_tot.get(k, 0.0) + v
+        total_ms += ms["layer"]
+        total_w += w.rows * w.cols
+        if (n + 1) % 7 == 0:
+            log(f"block {(n + 1) // 7}/{len(layers) // 7}: {total_ms:.1f} ms of quantization so far "
+                f"(inputs generated in {wall_gen:.1f} s)")
+    for pc in per_class.values():
+        pc["ms_per_layer"] = pc["ms"] / pc["layers"]
+    flops_h = sum(w.cols * (w.cols + 1) * w.tokens for w, _ in layers)
+    rec = {
+        "metric": METRIC,
+        "value": total_w / (total_ms / 1e3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 1,
+        "ms_per_step": total_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; per-linear N(0,0.02^2) weights and Student-t(4) activations, 0.5% outlier "
+                "channels x30)",
+        "config": {"workload": f"llama7b_decoder_sweep_{len(layers)}_linears", "blocks": len(layers) // 7,
+                   "linears": len(layers), "tokens": 262144, "bits": 4, "groupsize": 128, "blocksize": 128,
+                   "percdamp": 0.01, "act_order": False, "hadamard_rotation": bool(args.rotate)},
+        "sec_for_sweep": total_ms / 1e3,
+        "weights": total_w,
+        "hessian_tflops": flops_h / (stage_tot["hessian"] / 1e3) / 1e12,
+        "stage_ms_total": {k: round(v, 2) for k, v in stage_tot.items()},
+        "per_class": per_class,
+        "roofline": {
+            "kernel": "gptq_hessian_accumulate over the sweep (HIP events around each call)",
+            "bound": "mfma",
+            "achieved": flops_h / (stage_tot["hessian"] / 1e3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops_h / (stage_tot["hessian"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops_h / len(layers),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample of each layer shape ...")
+        sec = 0.0
+        samples = []
+        for w, li in {(lw.rows, lw.cols): (lw, i) for lw, i in layers}.values():
+            W, X = S.workload_device(w, layer=li, device=dev)
+            cb = cpu_baseline(W, X, w)
+            del W, X
+            n_cls = sum(1 for lw, _ in layers if (lw.rows, lw.cols) == (w.rows, w.cols))
+            sec += n_cls * cb["sec_per_layer_extrapolated"]
+            samples.append(f"{w.rows}x{w.cols} (x{n_cls}): {cb['sample']}")
+            cores = cb["cores"]
+        rec["cpu_baseline"] = {"value": total_w / sec, "unit": "weights/s", "cores": cores, "kind": "oracle",
+                               "sample": " | ".join(samples), "sec_for_sweep_extrapolated": sec}
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -577,6 +714,9 @@ def main(argv=None) -> int:
     ap.add_argument("--stack", action="store_true")
     ap.add_argument("--grid", action="store_true")
     ap.add_argument("--blocks", type=int, default=2)
+    ap.add_argument("--sweep", action="store_true", help="the 7B-shaped decoder sweep (224 linear layers)")
+    ap.add_argument("--sweep-blocks", type=int, default=32)
+    ap.add_argument("--rotate", action="store_true", help="--sweep: Hadamard pre-rotation of X and W")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -597,6 +737,8 @@ def main(argv=None) -> int:
         return bench_stack(args)
     if args.grid:
         return bench_grid(args)
+    if args.sweep:
+        return bench_sweep(args)
 
     from post_weight_quantization_23_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):

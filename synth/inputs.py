@@ -170,6 +170,24 @@ def activations_device(tokens: int, d: int, kind: str, outliers: int, gain: floa
     return out
 
 
+# The 7B-shaped decoder sweep: 32 blocks x 7 linear layers, 4-bit g128, each
+# linear with its own weights and its own calibration activations (seeded by
+# its position 7 * block + k), Student-t(4) with 0.5 % outlier channels x30.
+LLAMA7B_BLOCK = (("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+                 ("gate", 11008, 4096), ("up", 11008, 4096), ("down", 4096, 11008))
+
+
+def llama7b_sweep(blocks: int = 32):
+    """[(Workload, layer index)] for every linear of the sweep, in model order."""
+    out = []
+    for b in range(blocks):
+        for k, (name, r, c) in enumerate(LLAMA7B_BLOCK):
+            w = Workload(f"llama7b_sweep_{name}_{r}x{c}", 7, r, c, 262144, "bfloat16", "bfloat16", "t4",
+                         int(round(0.005 * c)), 30.0, 4, 128, 128, 0.01, False)
+            out.append((w, 7 * b + k))
+    return out
+
+
 def workload_device(w: Workload, layer: int = 0, tokens: int | None = None, device="cuda"):
     n = w.tokens if tokens is None else tokens
     W = weights_device(w.rows, w.cols, w.wid, layer, w.w_dtype, device)

@@ -38,6 +38,7 @@ FULL = [
     ("llama7b_up_11008x4096", True),      # 3-bit, act-order, 11008 rows
     ("llama7b_down_4096x11008", True),    # 3-bit, act-order, d = 11008, ReLU-sparse inputs
     ("opt175b_out_12288x12288", False),   # fp16, 3-bit, d = 12288
+    ("opt175b_fc2_12288x49152", False),   # fp16, 3-bit, d = 49152: H is 9.7 GB, d^2 > 2^31
 ]
 
 
@@ -49,11 +50,21 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def _sym(Hu):
-    Hu = np.triu(Hu)
-    return Hu + np.triu(Hu, 1).T
+def _sym(Hu, rows=4096):
+    """The symmetric matrix of an upper triangle, in place (the strictly
+    lower entries are overwritten), in slabs of rows so that no second
+    d x d array is made (d = 49152 is 19 GB in float64)."""
+    d = Hu.shape[0]
+    for s in range(0, d, rows):
+        e = min(d, s + rows)
+        blk = Hu[s:e, s:e]
+        il = np.tril_indices(e - s, -1)
+        blk[il] = blk.T[il]
+        Hu[s:e, :s] = Hu[:s, s:e].T
+    return Hu
 
 
+@pytest.mark.timeout(1500)
 @pytest.mark.parametrize("name,full_u", FULL)
 def test_full_size_layer(name, full_u):
     import post_weight_quantization_23_amd as q
@@ -88,8 +99,9 @@ def test_full_size_layer(name, full_u):
     torch.cuda.empty_cache()
 
     # ---- preparation
-    Hf = _sym(H.double().cpu().numpy())
+    Hf = _sym(H.cpu().numpy().astype(np.float64))
     del H
+    torch.cuda.empty_cache()
     Hd, perm_ref, dead_ref, _ = ref.prepare(Hf, w.percdamp, w.act_order)
     permg = perm.cpu().numpy().astype(np.int64)
     np.testing.assert_array_equal(permg, perm_ref)

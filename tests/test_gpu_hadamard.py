@@ -139,3 +139,45 @@ def test_rotation_full_size_x_sampled():
     rows = np.unique(np.concatenate([[0, 1, w.tokens - 1], rng.choice(w.tokens, 29, replace=False)]))
     rd = torch.from_numpy(rows).cuda()
     _check(Xr[rd].float().cpu().numpy(), X[rd].float().cpu().numpy(), 0, w.x_dtype)
+
+
+def test_gptq_on_a_rotated_layer():
+    """GPTQ after the Hadamard pre-rotation ("Post-Training Quantization:
+    Calibration, GPTQ and Why Rotations Help", "Rotations: making outliers
+    disappear"): X and W are rotated on the GPU along the input axis, then the
+    rotated layer goes through the whole path.  Checked against the oracle
+    run from the rotated tensors alone (its own H, factor and loop; objective
+    within 1e-3), and the rotated layer's objective measured in the original
+    space, ||W X - (W_hat_rot Q) X||^2, against the one in the rotated space
+    (the same number up to the single 16-bit rounding of X_rot and W_rot)."""
+    import post_weight_quantization_23_amd as q
+
+    r, d, n = 192, 512, 4096
+    W = torch.from_numpy(S.weights_host(r, d, 71, 0, "bfloat16")).cuda().to(torch.bfloat16)
+    X = torch.from_numpy(S.activations_host(n, d, "t4", outliers=4, gain=30.0, wid=71,
+                                            dtype="bfloat16")).cuda().to(torch.bfloat16)
+    Xr = q.hadamard_rotate(X)
+    Wr = q.hadamard_rotate(W)
+    outs = {}
+    for tag, WW, XX in (("plain", W, X), ("rotated", Wr, Xr)):
+        H = torch.zeros((d, d), dtype=torch.float32, device="cuda")
+        q.hessian_accumulate(H, XX)
+        perm, dead, _ = q.prepare(H, 0.01, False)
+        outs[tag] = q.quantize_layer(WW, H, perm, dead, bits=4, groupsize=128, blocksize=128, want_w_hat=True)
+    torch.cuda.synchronize()
+    Xh, Wh = X.float().cpu().numpy(), W.float().cpu().numpy().astype(np.float64)
+    Xrh, Wrh = Xr.float().cpu().numpy(), Wr.float().cpu().numpy().astype(np.float64)
+    # the oracle from the rotated tensors alone
+    Hr = ref.hessian(Xrh)
+    res = ref.gptq_quantize(Wrh, Hr, 4, 128, 0.01, False)
+    wh_rot = outs["rotated"]["w_hat"].cpu().numpy().astype(np.float64)
+    L_gpu, L_ref = ref.layer_loss(Wrh, wh_rot, Hr), ref.layer_loss(Wrh, res["w_hat"], Hr)
+    assert abs(L_gpu - L_ref) <= 1e-3 * L_ref, (L_gpu, L_ref)
+    # the same error seen in the original space: W_hat_rot Q acts on x
+    back = ref.hadamard_rotate(wh_rot)                   # Q is symmetric and its own inverse
+    L_orig = ref.layer_loss_from_x(Wh, back, Xh)
+    L_rot = ref.layer_loss_from_x(Wrh, wh_rot, Xrh)
+    L_plain = ref.layer_loss_from_x(Wh, outs["plain"]["w_hat"].cpu().numpy(), Xh)
+    print(f"\n  objective: rotated {L_rot:.6g} (original space {L_orig:.6g}), unrotated {L_plain:.6g}",
+          flush=True)
+    assert abs(L_orig - L_rot) <= 2e-2 * L_rot

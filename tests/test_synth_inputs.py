@@ -29,3 +29,13 @@ def test_workload_table_matches_stated_shapes():
     assert (t.rows, t.cols, t.tokens, t.groupsize, t.outliers) == (128, 256, 2048, -1, 4)
     assert round(0.005 * 4096) == S.WORKLOADS["llama7b_attn_4096x4096"].outliers
     assert round(0.001 * 49152) == S.WORKLOADS["opt175b_fc2_12288x49152"].outliers
+
+
+def test_decoder_sweep_table():
+    layers = S.llama7b_sweep()
+    assert len(layers) == 32 * 7
+    shapes = [(w.rows, w.cols) for w, _ in layers[:7]]
+    assert shapes == [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
+    assert [i for _, i in layers] == list(range(224))          # each linear its own seed
+    assert all(w.bits == 4 and w.groupsize == 128 and w.tokens == 262144 for w, _ in layers)
+    assert sum(w.rows * w.cols for w, _ in layers) == 32 * (4 * 4096 * 4096 + 3 * 11008 * 4096)
