@@ -7,9 +7,11 @@
 // fp32 and the sums are fp32 (v_mfma_f32_32x32x16_{bf16,f16}).
 //
 // Work split: 256 x 256 output tiles of the upper triangle, times `splits`
-// contiguous token ranges.  Each workgroup (4 waves, each a 128 x 128 block of
-// the tile as 4 x 4 MFMA blocks, accumulators in AGPRs) streams its token range
-// in K-steps of 64.  X arrives feature-contiguous (token rows), while an MFMA
+// contiguous token ranges.  Each workgroup streams its token range in K-steps
+// of 64; its waves hold blocks of the tile as 32 x 32 MFMA blocks with the
+// accumulators in AGPRs (8 waves of 128 x 64 on the LDS-direct path, two per
+// SIMD so that one wave's operand reads overlap the other's MFMAs; 4 waves of
+// 128 x 128 on the register path).  X arrives feature-contiguous (token rows), while an MFMA
 // operand wants 8 consecutive tokens of one feature.  Two data paths:
 //  * interior tiles (both 256-feature slabs inside [0, d), X 16-byte aligned,
 //    ldx % 8 == 0, ldx < 2^24): buffer loads that write LDS directly carry each
@@ -228,14 +230,17 @@ GPTQ_DEV void syrk_steps(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_
 // token rows of 512 bytes.
 GPTQ_DEV int dsw(int r) { return (r & 3) << 2; }
 
+constexpr int DMA_WAVES = 8;   // waves of the LDS-direct kernel: 2 x 4 blocks of 128 x 64
+constexpr int DMA_NB = 2;      // 32-column MFMA blocks per wave
+
 template <int DT, bool DIAG>
 GPTQ_DEV void syrk_steps_dma(const uint16_t* __restrict__ X, int64_t ldx, int64_t t_beg, int64_t t_end,
                              int fi0, int fj0, bool compute, int wm, int wn, unsigned char* smem,
-                             floatx16 (&acc)[4][4]) {
+                             floatx16 (&acc)[4][DMA_NB]) {
   constexpr int SLAB = KSTEP * 512, BUF = 2 * SLAB;
   // Each load instruction of a wave moves two token rows of one slab (32
-  // lanes x 16 bytes each); a wave issues 8 per slab and step.
-  constexpr int NI = KSTEP / 2 / 4;
+  // lanes x 16 bytes each); a wave issues 4 per slab and step.
+  constexpr int NI = KSTEP / 2 / DMA_WAVES;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   lds_u8* lbase = (lds_u8*)smem;  // generic to LDS address space
@@ -284,20 +289,20 @@ GPTQ_DEV void syrk_steps_dma(const uint16_t* __restrict__ X, int64_t ldx, int64_
     v[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
     return v;
   };
-  u32x4 fa[2][4], fb[2][4];
-  auto frags = [&](int b, int kk, u32x4 (&a)[4], u32x4 (&bb)[4]) {
+  u32x4 fa[2][4], fb[2][DMA_NB];
+  auto frags = [&](int b, int kk, u32x4 (&a)[4], u32x4 (&bb)[DMA_NB]) {
     const lds_u8* sa = lbase + b * BUF;
     const lds_u8* sb = DIAG ? sa : sa + SLAB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = frag(sa, wm + 32 * i, kk);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) bb[jj] = frag(sb, wn + 32 * jj, kk);
+    for (int jj = 0; jj < DMA_NB; ++jj) bb[jj] = frag(sb, wn + 32 * jj, kk);
   };
-  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&bb)[4]) {
+  auto mfmas = [&](const u32x4 (&a)[4], const u32x4 (&bb)[DMA_NB]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma16<DT>(a[i], bb[jj], acc[i][jj]);
+      for (int jj = 0; jj < DMA_NB; ++jj) acc[i][jj] = mfma16<DT>(a[i], bb[jj], acc[i][jj]);
   };
   if (nsteps <= 0) return;
   dma(0, 0);
@@ -322,24 +327,108 @@ GPTQ_DEV void syrk_steps_dma(const uint16_t* __restrict__ X, int64_t ldx, int64_
   }
 }
 
+// Work item of workgroup b.  Workgroup b runs on XCD b % 8; within each full
+// run of 256 workgroups it takes work item 32 (b % 8) + (b % 256) / 8 of that
+// run (a bijection).
+GPTQ_DEV int work_item(int b, int items) {
+  if (b < (items & ~255)) b = (b & ~255) | ((b & 7) << 5) | ((b & 255) >> 3);
+  return b;
+}
+
+// Epilogue of one wave's MB x NBW MFMA blocks at (wm, wn) of tile (fi0, fj0).
+// Lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] per block.  With one
+// split the tile is added into H, else written as the split's partial tile.
+template <int NBW>
+GPTQ_DEV void syrk_epilogue(const floatx16 (&acc)[4][NBW], bool compute, int wm, int wn, int fi0, int fj0, int d,
+                            float* __restrict__ H, float* __restrict__ part, int split, int tiles, int tile) {
+  const int lane = threadIdx.x & 63;
+  if (part == nullptr) {
+    if (!compute) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int gj = fj0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int gi = fi0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (gi < d && gj < d) {
+            float* p = H + (int64_t)gi * d + gj;
+            *p = __builtin_fmaf(2.0f, acc[i][j][v], *p);
+          }
+        }
+      }
+  } else {
+    float* pt = part + ((int64_t)split * tiles + tile) * (TILE * TILE);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) {
+        const int c = wn + 32 * j + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          pt[r * TILE + c] = compute ? acc[i][j][v] : 0.f;
+        }
+      }
+  }
+}
+
+// Interior tiles with 16-byte aligned X, ldx % 8 == 0 and ldx < 2^24: the
+// LDS-direct loop with 8 waves (2 per SIMD, so one wave's operand reads
+// overlap the other's matrix-core work), each a 128 x 64 block of the tile.
+// Work items whose tile is not interior are left to syrk16_kernel.
+template <int DT>
+__global__ __launch_bounds__(512, 1) void syrk16_dma_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                             int64_t n_tok, int d, int nt, int64_t chunk,
+                                                             float* __restrict__ H, float* __restrict__ part,
+                                                             int tiles, int splits) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int w = work_item((int)blockIdx.x, tiles * splits);
+  const int split = w / tiles, tile = w % tiles;
+  int bi, bj;
+  tile_coords(tile, nt, bi, bj);
+  const int fi0 = bi * TILE, fj0 = bj * TILE;
+  if (fi0 + TILE > d || fj0 + TILE > d) return;   // an edge tile: syrk16_kernel's
+  const bool diag = bi == bj;
+  const int64_t t_beg = (int64_t)split * chunk;
+  const int64_t t_end = min(n_tok, t_beg + chunk);
+  const int wave = threadIdx.x >> 6;
+  const int wm = (wave >> 2) * 128, wn = (wave & 3) * 64;
+  // On a diagonal tile the blocks strictly below the diagonal mirror ones
+  // above it and are not computed.
+  const bool compute = !(diag && wn + 64 <= wm);
+  floatx16 acc[4][DMA_NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < DMA_NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (diag) syrk_steps_dma<DT, true>(X, ldx, t_beg, t_end, fi0, fj0, compute, wm, wn, smem, acc);
+  else syrk_steps_dma<DT, false>(X, ldx, t_beg, t_end, fi0, fj0, compute, wm, wn, smem, acc);
+  syrk_epilogue<DMA_NB>(acc, compute, wm, wn, fi0, fj0, d, H, part, split, tiles, tile);
+}
+
+// The register path (edge tiles, or X without the alignment of the
+// LDS-direct path): 4 waves, each a 128 x 128 block of the tile.  With
+// skip_interior the interior tiles are left to syrk16_dma_kernel.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                          int64_t n_tok, int d, int nt,
                                                          int64_t chunk, float* __restrict__ H,
                                                          float* __restrict__ part, int tiles,
-                                                         int splits) {
+                                                         int splits, int skip_interior) {
   // LDS: A buffers 0/1 then B buffers 0/1, TILE rows of ROWB bytes each.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
-  // Workgroup b runs on XCD b % 8; within each full run of 256 workgroups it
-  // takes work item 32 (b % 8) + (b % 256) / 8 of that run (a bijection).
-  int w = (int)blockIdx.x;
-  if (w < ((tiles * splits) & ~255)) w = (w & ~255) | ((w & 7) << 5) | ((w & 255) >> 3);
+  const int w = work_item((int)blockIdx.x, tiles * splits);
   const int split = w / tiles, tile = w % tiles;
   int bi, bj;
   tile_coords(tile, nt, bi, bj);
   const bool diag = bi == bj;
   const int fi0 = bi * TILE, fj0 = bj * TILE;
+  if (skip_interior && fi0 + TILE <= d && fj0 + TILE <= d) return;
   const int64_t t_beg = (int64_t)split * chunk;
   const int64_t t_end = min(n_tok, t_beg + chunk);
 
@@ -358,48 +447,9 @@ __global__ __launch_bounds__(256, 1) void syrk16_kernel(const uint16_t* __restri
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // VEC: X 16-byte aligned, ldx % 8 == 0 and ldx < 2^24 (checked by the launcher).
-  const bool fast = VEC && fi0 + TILE <= d && fj0 + TILE <= d;
-  if (fast) {
-    if (diag) syrk_steps_dma<DT, true>(X, ldx, t_beg, t_end, fi0, fj0, compute, wm, wn, smem, acc);
-    else syrk_steps_dma<DT, false>(X, ldx, t_beg, t_end, fi0, fj0, compute, wm, wn, smem, acc);
-  } else {
-    if (diag) syrk_steps<DT, VEC, true>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc);
-    else syrk_steps<DT, VEC, false>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc);
-  }
-
-  // Epilogue.  Lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] per block.
-  if (part == nullptr) {
-    if (compute) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int gj = fj0 + wn + 32 * j + (lane & 31);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int gi = fi0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (gi < d && gj < d) {
-              float* p = H + (int64_t)gi * d + gj;
-              *p = __builtin_fmaf(2.0f, acc[i][j][v], *p);
-            }
-          }
-        }
-    }
-  } else {
-    float* pt = part + ((int64_t)split * tiles + tile) * (TILE * TILE);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = wn + 32 * j + (lane & 31);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          pt[r * TILE + c] = compute ? acc[i][j][v] : 0.f;
-        }
-      }
-  }
+  if (diag) syrk_steps<DT, VEC, true>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc);
+  else syrk_steps<DT, VEC, false>(X, ldx, t_beg, t_end, d, fi0, fj0, compute, wm, wn, smem, acc);
+  syrk_epilogue<4>(acc, compute, wm, wn, fi0, fj0, d, H, part, split, tiles, tile);
 }
 
 // H[i][j] += 2 * sum over splits of the partial tiles, in split order.  One
@@ -474,26 +524,41 @@ void launch_syrk16(float* H, int64_t d, const void* X, int dtype, int64_t n_tok,
   const int nt = (int)((d + TILE - 1) / TILE);
   const size_t shmem = 4 * TILE * ROWB;  // 128 KiB: A and B, double buffered
   static const bool attr_set = [&] {   // once, thread-safe (function-local static)
-    (void)hipFuncSetAttribute((const void*)syrk16_kernel<1, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    (void)hipFuncSetAttribute((const void*)syrk16_kernel<1, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    (void)hipFuncSetAttribute((const void*)syrk16_kernel<2, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    const void* fns[] = {(const void*)syrk16_kernel<1, true>, (const void*)syrk16_kernel<2, true>,
+                         (const void*)syrk16_kernel<1, false>, (const void*)syrk16_kernel<2, false>,
+                         (const void*)syrk16_dma_kernel<1>, (const void*)syrk16_dma_kernel<2>};
+    for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
     return true;
   }();
   (void)attr_set;
   dim3 grid((unsigned)(p.tiles * p.splits));
   float* part = p.splits > 1 ? ws : nullptr;
   const bool vec = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0) && ldx < (int64_t(1) << 24);
+  const bool edges = d % TILE != 0;   // tiles reaching past d take the register path
   const uint16_t* Xh = reinterpret_cast<const uint16_t*>(X);
+  // Interior tiles of aligned X: the 8-wave LDS-direct kernel; the rest (or
+  // everything, for X without that alignment): the register-path kernel.
+  // Each (split, tile) is computed by exactly one of the two, and both add
+  // the same products in the same order.
+  if (vec) {
+    if (dtype == 1)
+      hipLaunchKernelGGL((syrk16_dma_kernel<1>), grid, dim3(64 * DMA_WAVES), shmem, s, Xh, ldx, n_tok, (int)d, nt,
+                         p.chunk, H, part, p.tiles, p.splits);
+    else
+      hipLaunchKernelGGL((syrk16_dma_kernel<2>), grid, dim3(64 * DMA_WAVES), shmem, s, Xh, ldx, n_tok, (int)d, nt,
+                         p.chunk, H, part, p.tiles, p.splits);
+  }
+  if (!vec || edges) {
 #define GPTQ_SYRK_LAUNCH(DT, V)                                                                        \
   hipLaunchKernelGGL((syrk16_kernel<DT, V>), grid, dim3(256), shmem, s, Xh, ldx, n_tok, (int)d, nt, \
-                     p.chunk, H, part, p.tiles, p.splits)
-  if (dtype == 1) {
-    if (vec) GPTQ_SYRK_LAUNCH(1, true); else GPTQ_SYRK_LAUNCH(1, false);
-  } else {
-    if (vec) GPTQ_SYRK_LAUNCH(2, true); else GPTQ_SYRK_LAUNCH(2, false);
-  }
+                     p.chunk, H, part, p.tiles, p.splits, vec ? 1 : 0)
+    if (dtype == 1) {
+      if (vec) GPTQ_SYRK_LAUNCH(1, true); else GPTQ_SYRK_LAUNCH(1, false);
+    } else {
+      if (vec) GPTQ_SYRK_LAUNCH(2, true); else GPTQ_SYRK_LAUNCH(2, false);
+    }
 #undef GPTQ_SYRK_LAUNCH
+  }
   if (p.splits > 1) {
     const int64_t n4 = (int64_t)p.tiles * (TILE * TILE / 4);
     hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
