@@ -18,6 +18,7 @@ oracle timed on a bounded sample of the same workload.
     python bench.py --hadamard [--workload NAME] [--steps K] [--warmup W]
     python bench.py --stack [--blocks B] [--steps K] [--warmup W]
     python bench.py --sweep [--sweep-blocks 32] [--rotate]
+    python bench.py --hessian [--workload NAME] [--x-fill workload|uniform|zeros]
 
 --gemv measures the dequantizing matrix-vector product over packed layers
 instead: one step = one generated token (batch 1) through every linear layer
@@ -102,6 +103,8 @@ def cpu_baseline(W_dev, X_dev, w, tokens_sample=16384, rows_sample=128, cols_sam
     from oracle import gptq_ref as ref
 
     dc = min(w.cols, cols_sample)
+    tokens_sample = min(tokens_sample, w.tokens)
+    rows_sample = min(rows_sample, w.rows)
     X = X_dev[:tokens_sample, :dc].float().cpu().numpy()
     W = W_dev[:rows_sample, :dc].float().cpu().numpy()
     t0 = time.perf_counter()
@@ -700,6 +703,61 @@ def bench_sweep(args) -> int:
     return 0
 
 
+def bench_hessian(args) -> int:
+    """gptq_hessian_accumulate alone, back to back, on the workload's X or on
+    an X of the same shape filled with uniform random values in [-1, 1) or
+    zeros (the SYRK's clock depends on the operands' values)."""
+    import torch
+
+    from post_weight_quantization_23_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from post_weight_quantization_23_amd import build as b
+        b.build()
+    import post_weight_quantization_23_amd as q
+    from synth import inputs as S
+
+    w = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = getattr(torch, w.x_dtype)
+    if args.x_fill == "workload":
+        _, X = S.workload_device(w, device=dev)
+    else:
+        X = torch.empty((w.tokens, w.cols), dtype=dt, device=dev)
+        if args.x_fill == "zeros":
+            X.zero_()
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(S.torch_seed(w.wid, 0, 5))
+            X.uniform_(-1.0, 1.0, generator=g)
+    H = torch.zeros((w.cols, w.cols), dtype=torch.float32, device=dev)
+    ws = q.Workspace()
+    for _ in range(args.warmup):
+        q.hessian_accumulate(H, X, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        q.hessian_accumulate(H, X, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = w.cols * (w.cols + 1) * w.tokens
+    tf = flops / (ms / 1e3) / 1e12
+    peak = PEAK_FP16_TFLOPS if w.x_dtype == "float16" else PEAK_BF16_TFLOPS
+    print(json.dumps({
+        "metric": "Hessian TFLOP/s (gptq_hessian_accumulate alone)", "value": tf, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.x_dtype == "bfloat16" else "fp16",
+        "data": f"synthetic ({args.x_fill} activations)",
+        "config": {"workload": w.name, "cols": w.cols, "tokens": w.tokens, "x_fill": args.x_fill},
+        "roofline": {"kernel": "syrk16_dma_kernel + reduce_partials_kernel", "bound": "mfma", "achieved": tf,
+                     "peak": peak, "unit": "TFLOP/s", "frac": tf / peak, "traffic": None,
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -717,6 +775,9 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true", help="the 7B-shaped decoder sweep (224 linear layers)")
     ap.add_argument("--sweep-blocks", type=int, default=32)
     ap.add_argument("--rotate", action="store_true", help="--sweep: Hadamard pre-rotation of X and W")
+    ap.add_argument("--hessian", action="store_true", help="gptq_hessian_accumulate alone, back to back")
+    ap.add_argument("--x-fill", default="workload", choices=["workload", "uniform", "zeros"],
+                    help="--hessian: the workload's X, or uniform random / zero values of its shape")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -739,6 +800,8 @@ def main(argv=None) -> int:
         return bench_grid(args)
     if args.sweep:
         return bench_sweep(args)
+    if args.hessian:
+        return bench_hessian(args)
 
     from post_weight_quantization_23_amd import _lib
     if not os.path.exists(_lib.LIB_PATH):
