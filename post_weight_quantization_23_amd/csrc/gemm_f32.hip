@@ -61,6 +61,34 @@ GPTQ_DEV floatx4 load4(const float* base, int64_t ld, int row, int col, int rows
   return v;
 }
 
+// Output tile of workgroup `bid` (tiles of TM x TN).  With upper_only (a
+// square problem, TM == TN) only the tiles on and above the diagonal are
+// numbered, row by row.  Otherwise a triangular operand gives tiles K-ranges
+// of different lengths (see the kernels' k_lo / k_hi), and the tiles are
+// numbered longest first along the index that sets the length: the
+// dispatcher hands consecutive workgroups to different CUs, so each CU gets
+// a mix of long and short tiles instead of one CU getting all the long ones.
+GPTQ_DEV void tile_of(const GemmArgs& g, int bid, int TM, int TN, int& bm, int& bn) {
+  const int tm = (g.M + TM - 1) / TM, tn = (g.N + TN - 1) / TN;
+  if (g.upper_only) {
+    int r = 0;
+    while (r < tm - 1 && bid >= tn - r) {
+      bid -= tn - r;
+      ++r;
+    }
+    bm = r;
+    bn = r + bid;
+  } else if (g.b_mask != MASK_NONE && g.a_mask == MASK_NONE) {
+    const int sl = bid / tm;
+    bm = bid % tm;
+    bn = g.b_mask == MASK_LOWER ? sl : tn - 1 - sl;   // LOWER: k >= n - off, long for small n
+  } else {
+    const int sl = bid / tn;
+    bn = bid % tn;
+    bm = g.a_mask == MASK_LOWER ? tm - 1 - sl : sl;   // UPPER: k >= m - off, long for small m
+  }
+}
+
 struct GemmPair {
   GemmArgs g[2];
   int tiles0;   // tiles of g[0]; workgroups from here on belong to g[1]
@@ -79,10 +107,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmPair pr) {
   const bool second = (int)blockIdx.x >= pr.tiles0;
   const GemmArgs& g = second ? pr.g[1] : pr.g[0];
   const int bid = second ? (int)blockIdx.x - pr.tiles0 : (int)blockIdx.x;
-  const int tiles_n = (g.N + TN - 1) / TN;
-  const int bm = bid / tiles_n, bn = bid % tiles_n;
+  int bm, bn;
+  tile_of(g, bid, TM, TN, bm, bn);
   const int m0 = bm * TM, n0 = bn * TN;
-  if (g.upper_only && n0 + TN <= m0) return;  // tile strictly below the diagonal
 
   // K range that can hold non-zero products for this tile.
   int k_lo = 0, k_hi = g.K;
@@ -373,10 +400,9 @@ __global__ __launch_bounds__(256) void gemm_f32_dma_kernel(GemmPair pr) {
   const bool second = (int)blockIdx.x >= pr.tiles0;
   const GemmArgs& g = second ? pr.g[1] : pr.g[0];
   const int bid = second ? (int)blockIdx.x - pr.tiles0 : (int)blockIdx.x;
-  const int tiles_n = (g.N + TN - 1) / TN;
-  const int bm = bid / tiles_n, bn = bid % tiles_n;
+  int bm, bn;
+  tile_of(g, bid, TM, TN, bm, bn);
   const int m0 = bm * TM, n0 = bn * TN;
-  if (g.upper_only && n0 + TN <= m0) return;  // tile strictly below the diagonal
 
   int k_lo = 0, k_hi = g.K;
   if (g.a_mask == MASK_UPPER) k_lo = max(k_lo, m0 - g.a_off);
@@ -444,9 +470,9 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmPair pr) {
   const bool second = (int)blockIdx.x >= pr.tiles0;
   const GemmArgs& g = second ? pr.g[1] : pr.g[0];
   const int bid = second ? (int)blockIdx.x - pr.tiles0 : (int)blockIdx.x;
-  const int tiles_n = (g.N + 31) / 32;
-  const int m0 = (bid / tiles_n) * 32, n0 = (bid % tiles_n) * 32;
-  if (g.upper_only && n0 + 32 <= m0) return;
+  int bm, bn;
+  tile_of(g, bid, 32, 32, bm, bn);
+  const int m0 = bm * 32, n0 = bn * 32;
   __shared__ floatx16 red[3][64];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -507,9 +533,14 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmPair pr) {
   }
 }
 
+// Workgroups of a problem: every tile, or with upper_only (M == N, square
+// tiles) the tiles on and above the diagonal only.
 template <int TM, int TN, int KT>
 int64_t tiles_of(const GemmArgs& g) {
-  return (g.M <= 0 || g.N <= 0) ? 0 : (int64_t)((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN);
+  static_assert(TM == TN, "upper_only numbering assumes square tiles");
+  if (g.M <= 0 || g.N <= 0) return 0;
+  const int64_t tm = (g.M + TM - 1) / TM, tn = (g.N + TN - 1) / TN;
+  return g.upper_only ? tm * (tm + 1) / 2 : tm * tn;
 }
 
 // Operands the LDS-direct kernel can take: 16-byte aligned, rows of a whole
