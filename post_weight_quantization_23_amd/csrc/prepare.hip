@@ -130,47 +130,70 @@ __global__ __launch_bounds__(256) void zero_lower_kernel(float* H, int64_t d) {
 //   factor : V[:, j] = A[:, j] / sqrt(A[j][j]);  A[0:j, 0:j] -= V[0:j, j] V[0:j, j]^T
 //   invert : X[j, :] /= V[j][j];  X[0:j, :] -= V[0:j, j] X[j, :]   (X starts as I)
 // (row j of X is final at step j: every later row has already been removed).
-// Registers only: lane k < S holds column k of the symmetric block A, lane
-// S + c column c of X (lanes from 2S on idle).  With p = A[j][j] and a_i =
-// A[i][j] (read from lane j), both updates are  col[i] -= a_i * col[j] / p  for
-// i < j -- on the A side col[j] = A[j][k] = A[k][j] by symmetry, on the X side
-// col[j] = X[j][c] before its scaling -- and the X side then scales col[j] by
-// 1/sqrt(p).  A non-positive or NaN pivot is recorded as the sweep goes (the
-// first one found, a wave-uniform value) and reported once at the end.
+// Registers only: lane k of a 16-lane row holds column k of the symmetric
+// block A and column k of X.  With p = A[j][j] and a_i = A[i][j] (lane j's
+// A[i]), both updates are  col[i] -= a_i * col[j] / p  for i < j -- on the A
+// side col[j] = A[j][k] = A[k][j] by symmetry, on the X side col[j] = X[j][k]
+// before its scaling -- and the X side then scales col[j] by 1/sqrt(p).  A
+// non-positive or NaN pivot is recorded as the sweep goes (the first one
+// found) and reported once at the end.
 template <int S>
 __device__ __forceinline__ void leaf_sweep(float* M, int o, int32_t* info, int64_t gbase, int pad) {
+  static_assert(S == 16, "the row broadcast spans 16 lanes");
+  // Every 16-lane row of the wave holds the symmetric block, lane k of a row
+  // column k (col[i] = A[i][k]); row 1 also holds X (lane 16 + c: column c).
+  // A[i][j] reaches every lane of a row from its lane j by a DPP row
+  // broadcast, so each row updates its own copy without leaving the VALU.
   const int lane = threadIdx.x & 63;
-  const int k = lane % S;
-  const bool xside = lane >= S && lane < 2 * S;
-  const bool active = lane < 2 * S;
-  float col[S];
+  const int k = lane & 15;
+  const bool xside = (lane >> 4) == 1;
+  float col[S], xc[S];
 #pragma unroll
   for (int i = 0; i < S; ++i) {
-    const float av = M[(o + min(i, k)) * LDM + o + max(i, k)];
-    col[i] = xside ? (i == k ? 1.f : 0.f) : av;
+    col[i] = M[(o + min(i, k)) * LDM + o + max(i, k)];
+    xc[i] = i == k ? 1.f : 0.f;
   }
+  // row_newbcast: lane src of each 16-lane row to the whole row (src is a
+  // constant in every unrolled step, so the switch folds away)
+  auto bc = [](float v, int src) {
+    const int iv = __float_as_int(v);
+    int r;
+    switch (src) {
+#define GPTQ_RB(n) \
+  case n: r = __builtin_amdgcn_mov_dpp(iv, 0x150 + n, 0xF, 0xF, true); break;
+      GPTQ_RB(0) GPTQ_RB(1) GPTQ_RB(2) GPTQ_RB(3) GPTQ_RB(4) GPTQ_RB(5) GPTQ_RB(6) GPTQ_RB(7)
+      GPTQ_RB(8) GPTQ_RB(9) GPTQ_RB(10) GPTQ_RB(11) GPTQ_RB(12) GPTQ_RB(13) GPTQ_RB(14)
+      default: r = __builtin_amdgcn_mov_dpp(iv, 0x150 + 15, 0xF, 0xF, true); break;
+#undef GPTQ_RB
+    }
+    return __int_as_float(r);
+  };
   int bad = -1;   // sweep position of the first non-positive pivot found
 #pragma unroll
   for (int j = S - 1; j >= 0; --j) {
-    const float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(col[j]), j));
-    bad = (bad < 0 && !(piv > 0.f)) ? j : bad;
+    const float piv = bc(col[j], j);
     const float rv = __builtin_amdgcn_rsqf(piv);   // 1/sqrt(pivot), ~1 ulp
-    const float f = col[j] * (rv * rv);
+    const float inv = rv * rv;
+    const float fa = col[j] * inv, fx = xc[j] * inv;
+    {
+      const float ps = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(piv)));
+      bad = (bad < 0 && !(ps > 0.f)) ? j : bad;
+    }
 #pragma unroll
     for (int i = 0; i < j; ++i) {
-      const float ai = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(col[i]), j));
-      col[i] = __builtin_fmaf(-ai, f, col[i]);
+      const float ai = bc(col[i], j);
+      col[i] = __builtin_fmaf(-ai, fa, col[i]);
+      xc[i] = __builtin_fmaf(-ai, fx, xc[i]);
     }
-    if (xside) col[j] *= rv;
+    xc[j] *= rv;
   }
   if (xside) {
 #pragma unroll
-    for (int i = 0; i < S; ++i) M[(o + i) * LDM + o + k] = (k >= i) ? col[i] : 0.f;
+    for (int i = 0; i < S; ++i) M[(o + i) * LDM + o + k] = (k >= i) ? xc[i] : 0.f;
   }
   if (lane == 0 && bad >= 0 && (o + bad) >= pad) {
     if (*info == 0) *info = (int32_t)(gbase + (o + bad - pad) + 1);
   }
-  (void)active;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
