@@ -33,6 +33,32 @@ __global__ __launch_bounds__(256) void pack4_kernel(const uint8_t* __restrict__ 
   out[row * ldw + wd] = w;
 }
 
+// 4-bit, 32 codes per thread: two 16-byte loads, one 16-byte store of four
+// words (rows of codes and of words 16-byte aligned, c % 32 == 0).
+__global__ __launch_bounds__(256) void pack4x4_kernel(const uint8_t* __restrict__ codes, int64_t r,
+                                                      int64_t c, uint32_t* __restrict__ out, int64_t ldw) {
+  const int64_t qpr = c / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= r * qpr) return;
+  const int64_t row = idx / qpr, qd = idx % qpr;
+  const u32x4* src = reinterpret_cast<const u32x4*>(codes + row * c + qd * 32);
+  const u32x4 a = __builtin_nontemporal_load(src), b = __builtin_nontemporal_load(src + 1);
+  const uint32_t in[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 o;
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t x = in[2 * wd], y = in[2 * wd + 1];
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w |= ((x >> (8 * k)) & 0xFu) << (4 * k);
+      w |= ((y >> (8 * k)) & 0xFu) << (4 * (k + 4));
+    }
+    o[wd] = w;
+  }
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + row * ldw + qd * 4));
+}
+
 __global__ __launch_bounds__(256) void pack3_kernel(const uint8_t* __restrict__ codes, int64_t r,
                                                     int64_t c, uint32_t* __restrict__ out,
                                                     int64_t ldw) {
@@ -99,7 +125,12 @@ void launch_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, const int
                        bits, perm, packed, ld_words);
     return;
   }
-  if (bits == 4) {
+  const bool wide = (c % 32 == 0) && (ld_words % 4 == 0) && (reinterpret_cast<uintptr_t>(packed) % 16 == 0);
+  if (bits == 4 && wide) {
+    const int64_t n = r * (c / 32);
+    hipLaunchKernelGGL(pack4x4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, r, c,
+                       packed, ld_words);
+  } else if (bits == 4) {
     const int64_t n = r * (c / 8);
     hipLaunchKernelGGL(pack4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, r, c,
                        packed, ld_words);

@@ -112,7 +112,7 @@ def stagewise(W_host, H_gpu, bits, groupsize, blocksize, act_order, percdamp=0.0
 
 
 # ----------------------------------------------------------------------- pack
-@pytest.mark.parametrize("bits,r,c", [(4, 37, 256), (4, 1, 8), (3, 19, 96), (3, 2, 32)])
+@pytest.mark.parametrize("bits,r,c", [(4, 37, 256), (4, 1, 8), (4, 5, 40), (3, 19, 96), (3, 2, 32)])
 def test_pack_matches_oracle(bits, r, c):
     rng = np.random.default_rng(100 + bits)
     codes = rng.integers(0, 2 ** bits, size=(r, c)).astype(np.uint8)
@@ -120,6 +120,22 @@ def test_pack_matches_oracle(bits, r, c):
     torch.cuda.synchronize()
     got = words.cpu().numpy().view(np.uint32) if words.dtype != torch.uint32 else words.cpu().numpy()
     np.testing.assert_array_equal(got.astype(np.uint64), ref.pack_codes(codes, bits).astype(np.uint64))
+
+
+def test_pack4_word_paths_agree():
+    """4-bit packing: 32 codes per thread into 16-byte stores (aligned rows of
+    words, c % 32 == 0) and one word per thread (any other layout) give the
+    same words."""
+    rng = np.random.default_rng(104)
+    r, c = 29, 320
+    codes = torch.from_numpy(rng.integers(0, 16, size=(r, c)).astype(np.uint8)).cuda()
+    wide = gq().pack(codes, 4)
+    odd = torch.zeros((r, c // 8 + 1), dtype=torch.int32, device="cuda")[:, : c // 8]   # ld_words odd
+    gq().pack(codes, 4, out=odd.view(torch.uint32))
+    torch.cuda.synchronize()
+    assert torch.equal(wide.view(torch.int32), odd.contiguous())
+    np.testing.assert_array_equal(wide.cpu().numpy().view(np.uint32).astype(np.uint64),
+                                  ref.pack_codes(codes.cpu().numpy(), 4).astype(np.uint64))
 
 
 # -------------------------------------------------------------------- Hessian
