@@ -402,34 +402,21 @@ GPTQ_DEV bool run_chain(const BlockArgs& a, const float* Vl, int p, int64_t row,
 // MIDG: groups shorter than the block also start inside it (32: their width
 // is a multiple of 32; -1: any width; 0: none).  FULL: the
 // block has all BMAX columns.
+// One block's columns for this thread's row (V and invd staged): the chain
+// (fast decisions; repeated exactly from the block's starting values w0 when
+// any decision of the wave is doubtful), then codes, w_hat and scaled errors
+// e = (w - w_hat) / U_jj, stored at the original columns, E in row-major
+// block order, and the row's loss.  w ends holding each column's value at its
+// turn; ereg the scaled errors.
 template <int L, int MIDG, bool FULL>
-__global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
-  constexpr int S = BMAX / L;          // slots per lane
-  constexpr int ROWS = 256 / L;        // rows per workgroup
-  __shared__ __attribute__((aligned(16))) float Vl[BMAX * BMAX];
-  __shared__ float invd[BMAX];
-
-  const int tid = threadIdx.x;
-  const int p = tid % L;
-  const int64_t row = (int64_t)blockIdx.x * ROWS + tid / L;
-  const bool valid = row < a.r;
+GPTQ_DEV void block_columns(const BlockArgs& a, const float* Vl, const float* invd, int p, int64_t row, bool valid,
+                            const float* Wrow, float (&w)[BMAX / L], const float (&w0)[BMAX / L],
+                            float (&ereg)[BMAX / L]) {
+  constexpr int S = BMAX / L;
   const int Bw = FULL ? BMAX : a.Bw;
   const int64_t i1 = a.i1, c = a.c;
-  const float* Wrow = a.Wp + (valid ? row : 0) * c;
   const float maxq = (float)((1 << a.bits) - 1);
-
-  float w[S];
-  auto load_w = [&]() {
-#pragma unroll
-    for (int m = 0; m < S; ++m) {
-      const int col = p + L * m;
-      w[m] = (valid && col < Bw) ? Wrow[i1 + col] : 0.f;
-    }
-  };
-  load_w();
-  stage_block(a, Vl, invd, FULL);
-
-  float qreg[S], ereg[S], whreg[S];
+  float qreg[S], whreg[S];
 #pragma unroll
   for (int m = 0; m < S; ++m) qreg[m] = ereg[m] = whreg[m] = 0.f;
   float scale = 1.f, zero = 0.f;
@@ -441,7 +428,8 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
   }
   const bool exact = __ballot(bad) != 0;   // wave-uniform
   if (exact) {                              // repeat this wave's rows exactly
-    load_w();
+#pragma unroll
+    for (int m = 0; m < S; ++m) w[m] = w0[m];
     run_chain<L, MIDG, FULL, true>(a, Vl, p, row, valid, Wrow, w, qreg, ereg, whreg, scale, zero);
   }
   if constexpr (MIDG == 0) {
@@ -480,6 +468,109 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
     }
   }
   if (p == 0 && a.row_loss) a.row_loss[row] += loss;
+}
+
+template <int L, int MIDG, bool FULL>
+__global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
+  constexpr int S = BMAX / L;          // slots per lane
+  constexpr int ROWS = 256 / L;        // rows per workgroup
+  __shared__ __attribute__((aligned(16))) float Vl[BMAX * BMAX];
+  __shared__ float invd[BMAX];
+
+  const int tid = threadIdx.x;
+  const int p = tid % L;
+  const int64_t row = (int64_t)blockIdx.x * ROWS + tid / L;
+  const bool valid = row < a.r;
+  const int Bw = FULL ? BMAX : a.Bw;
+  const float* Wrow = a.Wp + (valid ? row : 0) * a.c;
+
+  float w[S], w0[S], ereg[S];
+#pragma unroll
+  for (int m = 0; m < S; ++m) {
+    const int col = p + L * m;
+    w[m] = w0[m] = (valid && col < Bw) ? Wrow[a.i1 + col] : 0.f;
+  }
+  stage_block(a, Vl, invd, FULL);
+  block_columns<L, MIDG, FULL>(a, Vl, invd, p, row, valid, Wrow, w, w0, ereg);
+}
+
+// A super-block of SB_BLOCKS full blocks in one launch (16 lanes per row, 16
+// rows per workgroup, groups of one block or one ruler per row): the row's
+// 512 columns stay in registers from the first block to the last.  After
+// each block, its scaled errors E (16 rows x 128, through LDS) update the
+// super-block's later blocks on the matrix cores,
+//     W[:, k'] -= E_k U[block k, block k'],
+// with v_mfma_f32_16x16x4f32 (M = the 16 rows, N = 128, K = 128; each wave
+// two 16-column tiles, U read from memory), the product going back to the
+// rows' lanes through LDS.  The E of all blocks is also stored for the
+// deferred product beyond the super-block.
+constexpr int SB_BLOCKS = 4;
+constexpr int EPAD = BMAX + 4;   // LDS row stride of the E and product tiles
+
+__global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1) {
+  constexpr int L = 16, S = BMAX / L, ROWS = 16;
+  __shared__ __attribute__((aligned(16))) float Vl[BMAX * BMAX];
+  __shared__ float invd[BMAX];
+  __shared__ float Et[ROWS * EPAD];   // scaled errors of the block just done
+  __shared__ float Pt[ROWS * EPAD];   // E_k U[k, k'] for one later block k'
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = tid % L, rl = tid / L;
+  const int64_t row = (int64_t)blockIdx.x * ROWS + rl;
+  const bool valid = row < a.r;
+  const int64_t c = a.c;
+  const float* Wrow = a.Wp + (valid ? row : 0) * c;
+
+  float wsb[SB_BLOCKS][S];
+#pragma unroll
+  for (int kb = 0; kb < SB_BLOCKS; ++kb)
+#pragma unroll
+    for (int m = 0; m < S; ++m) wsb[kb][m] = valid ? Wrow[s1 + BMAX * kb + p + L * m] : 0.f;
+
+  float* E0 = a.E;
+#pragma unroll
+  for (int kb = 0; kb < SB_BLOCKS; ++kb) {
+    BlockArgs b = a;
+    b.i1 = s1 + BMAX * kb;
+    b.Bw = BMAX;
+    b.E = E0 + BMAX * kb;
+    stage_block(b, Vl, invd, true);
+    float w[S], ereg[S];
+#pragma unroll
+    for (int m = 0; m < S; ++m) w[m] = wsb[kb][m];
+    block_columns<16, 0, true>(b, Vl, invd, p, row, valid, Wrow, w, wsb[kb], ereg);
+    if (kb + 1 < SB_BLOCKS) {
+#pragma unroll
+      for (int m = 0; m < S; ++m) Et[rl * EPAD + p + L * m] = ereg[m];   // 0 on rows past r
+      __syncthreads();
+      // A operand for every later block: lane l gives E[l % 16][4 s + l / 16].
+      float ea[BMAX / 4];
+#pragma unroll
+      for (int s4 = 0; s4 < BMAX / 4; ++s4) ea[s4] = Et[(lane & 15) * EPAD + 4 * s4 + (lane >> 4)];
+#pragma unroll
+      for (int kb2 = kb + 1; kb2 < SB_BLOCKS; ++kb2) {
+        // wave w: columns 32 w .. 32 w + 31 of block kb2 (two 16-column tiles)
+        const float* Ub = a.U + (b.i1 + (lane >> 4)) * c + s1 + BMAX * kb2 + 32 * wave + (lane & 15);
+        floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < BMAX / 4; ++s4) {
+          const float u0 = Ub[(int64_t)(4 * s4) * c], u1 = Ub[(int64_t)(4 * s4) * c + 16];
+          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[s4], u0, d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[s4], u1, d1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = 4 * (lane >> 4) + v;
+          Pt[i * EPAD + 32 * wave + (lane & 15)] = d0[v];
+          Pt[i * EPAD + 32 * wave + 16 + (lane & 15)] = d1[v];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < S; ++m) wsb[kb2][m] -= Pt[rl * EPAD + p + L * m];
+        __syncthreads();
+      }
+    }
+  }
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -564,8 +655,20 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   // groups shorter than the block: width a multiple of 32 (32), any (-1)
   const int midg = !(a.groupsize > 0 && a.groupsize < B) ? 0 : (a.groupsize % 32 == 0) ? 32 : -1;
   const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
+  // Whole super-blocks of four full blocks, with 16 lanes per row and rulers
+  // per row or per block, run as one launch each.
+  const bool sb_ok = wide && midg == 0 && B == BMAX && SB == SB_BLOCKS * BMAX &&
+                     (a.groupsize <= 0 || a.groupsize == BMAX);
   for (int64_t s1 = 0; s1 < c; s1 += SB) {
     const int64_t s2 = std::min(s1 + SB, c);
+    if (sb_ok && s2 - s1 == SB) {
+      b.i1 = s1;
+      b.Bw = BMAX;
+      b.E = E;
+      hipLaunchKernelGGL(superblock_kernel, g16, dim3(256), 0, s, b, s1);
+      if (s2 < c) gemm_update(s, r, c, E, SB, (int)(s2 - s1), a.U, s1, s2, c, Wp);
+      continue;
+    }
     for (int64_t i1 = s1; i1 < s2; i1 += B) {
       const int Bw = (int)std::min<int64_t>(B, s2 - i1);
       const int64_t i2 = i1 + Bw;

@@ -256,6 +256,7 @@ CASES = [
     (1040, 256, 4, 32, 128, False, 2, "float16"),    # 16 lanes, four groups per full block
     (20, 300, 4, 256, 128, False, 0, "float32"),     # group spanning two blocks
     (1030, 1100, 4, 128, 128, True, 2, "bfloat16"),  # several super-blocks, ragged tail
+    (1024, 1536, 3, -1, 128, False, 1, "float16"),   # one ruler per row, three whole super-blocks
     (70, 1300, 3, 256, 64, False, 0, "float16"),     # groups of 4 blocks across super-blocks
 ]
 
