@@ -501,15 +501,67 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
 // super-block's later blocks on the matrix cores,
 //     W[:, k'] -= E_k U[block k, block k'],
 // with v_mfma_f32_16x16x4f32 (M = the 16 rows, N = 128, K = 128; each wave
-// two 16-column tiles, U read from memory), the product going back to the
-// rows' lanes through LDS.  The E of all blocks is also stored for the
-// deferred product beyond the super-block.
+// two 16-column tiles), the product going back to the rows' lanes through
+// LDS.  The E of all blocks is also stored for the deferred product beyond
+// the super-block.
+//
+// Every 128 x 128 tile of U the workgroup needs -- the next update's tile of
+// U, or the next block's corner -- is loaded into registers one phase ahead
+// (16 float4 per thread, all in flight at once) and written to the one LDS
+// tile buffer when its phase comes, so the loads of the first update run
+// under the chain and each later load under the previous phase.
 constexpr int SB_BLOCKS = 4;
 constexpr int EPAD = BMAX + 4;   // LDS row stride of the E and product tiles
+constexpr int TPAD = BMAX + 4;   // LDS row stride of a tile of U in an update (4 rows of an
+                                 // MFMA operand read land on different banks)
+
+// Thread t's share of the 128 x 128 tile of U at (i0, j0): rows t / 32 + 8u,
+// columns 4 (t % 32) .. +3 (U 16-byte aligned, c % 4 == 0), and for t < 128
+// the diagonal U[i0 + t][i0 + t] (used when the tile is a block's corner).
+struct TileRegs {
+  floatx4 v[16];
+  float dg;
+};
+
+GPTQ_DEV void tile_issue(const float* U, int64_t c, int64_t i0, int64_t j0, TileRegs& t) {
+  const int tid = threadIdx.x;
+  const float* ub = U + (i0 + (tid >> 5)) * c + j0 + (tid & 31) * 4;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) t.v[u] = *reinterpret_cast<const floatx4*>(ub + (int64_t)(8 * u) * c);
+  t.dg = tid < BMAX ? U[(i0 + tid) * c + (i0 + tid)] : 1.f;
+}
+
+// The tile as it is (row-major 128 x 128, row stride TPAD), for an update.
+GPTQ_DEV void tile_commit_raw(const TileRegs& t, float* Tl) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e4 = tid + 256 * u;
+    *reinterpret_cast<floatx4*>(Tl + (e4 >> 5) * TPAD + (e4 & 31) * 4) = t.v[u];
+  }
+}
+
+// The tile as a block's V = U / diag(U), zero on and left of the diagonal
+// (the layout stage_block writes), and invd = 1 / U_jj.
+GPTQ_DEV void tile_commit_corner(const TileRegs& t, float* Vl, float* invd) {
+  const int tid = threadIdx.x;
+  if (tid < BMAX) invd[tid] = __fdiv_rn(1.0f, t.dg);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e4 = tid + 256 * u, j = e4 >> 5, k = (e4 & 31) * 4;
+    const float sj = invd[j];
+    floatx4 o;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) o[cc] = (k + cc > j) ? t.v[u][cc] * sj : 0.f;
+    *reinterpret_cast<floatx4*>(Vl + j * BMAX + k) = o;
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1) {
   constexpr int L = 16, S = BMAX / L, ROWS = 16;
-  __shared__ __attribute__((aligned(16))) float Vl[BMAX * BMAX];
+  __shared__ __attribute__((aligned(16))) float Vl[BMAX * TPAD];   // a block's V, or a tile of U
   __shared__ float invd[BMAX];
   __shared__ float Et[ROWS * EPAD];   // scaled errors of the block just done
   __shared__ float Pt[ROWS * EPAD];   // E_k U[k, k'] for one later block k'
@@ -521,11 +573,14 @@ __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1
   const int64_t c = a.c;
   const float* Wrow = a.Wp + (valid ? row : 0) * c;
 
+  TileRegs tr;
+  tile_issue(a.U, c, s1, s1, tr);   // the first block's corner
   float wsb[SB_BLOCKS][S];
 #pragma unroll
   for (int kb = 0; kb < SB_BLOCKS; ++kb)
 #pragma unroll
     for (int m = 0; m < S; ++m) wsb[kb][m] = valid ? Wrow[s1 + BMAX * kb + p + L * m] : 0.f;
+  tile_commit_corner(tr, Vl, invd);
 
   float* E0 = a.E;
 #pragma unroll
@@ -534,7 +589,8 @@ __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1
     b.i1 = s1 + BMAX * kb;
     b.Bw = BMAX;
     b.E = E0 + BMAX * kb;
-    stage_block(b, Vl, invd, true);
+    // the first update's tile of U, in flight during the chain
+    if (kb + 1 < SB_BLOCKS) tile_issue(a.U, c, b.i1, b.i1 + BMAX, tr);
     float w[S], ereg[S];
 #pragma unroll
     for (int m = 0; m < S; ++m) w[m] = wsb[kb][m];
@@ -542,21 +598,25 @@ __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1
     if (kb + 1 < SB_BLOCKS) {
 #pragma unroll
       for (int m = 0; m < S; ++m) Et[rl * EPAD + p + L * m] = ereg[m];   // 0 on rows past r
-      __syncthreads();
+      __syncthreads();   // E complete; every wave is done with V
       // A operand for every later block: lane l gives E[l % 16][4 s + l / 16].
       float ea[BMAX / 4];
 #pragma unroll
       for (int s4 = 0; s4 < BMAX / 4; ++s4) ea[s4] = Et[(lane & 15) * EPAD + 4 * s4 + (lane >> 4)];
 #pragma unroll
       for (int kb2 = kb + 1; kb2 < SB_BLOCKS; ++kb2) {
+        tile_commit_raw(tr, Vl);   // U[block kb, block kb2]
+        // next phase's tile: the next update's, or the next block's corner
+        if (kb2 + 1 < SB_BLOCKS) tile_issue(a.U, c, b.i1, s1 + BMAX * (kb2 + 1), tr);
+        else tile_issue(a.U, c, b.i1 + BMAX, b.i1 + BMAX, tr);
+        __syncthreads();
         // wave w: columns 32 w .. 32 w + 31 of block kb2 (two 16-column tiles)
-        const float* Ub = a.U + (b.i1 + (lane >> 4)) * c + s1 + BMAX * kb2 + 32 * wave + (lane & 15);
+        const float* Ut = Vl + (lane >> 4) * TPAD + 32 * wave + (lane & 15);
         floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s4 = 0; s4 < BMAX / 4; ++s4) {
-          const float u0 = Ub[(int64_t)(4 * s4) * c], u1 = Ub[(int64_t)(4 * s4) * c + 16];
-          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[s4], u0, d0, 0, 0, 0);
-          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[s4], u1, d1, 0, 0, 0);
+          d0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[s4], Ut[4 * s4 * TPAD], d0, 0, 0, 0);
+          d1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ea[s4], Ut[4 * s4 * TPAD + 16], d1, 0, 0, 0);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
@@ -567,8 +627,8 @@ __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < S; ++m) wsb[kb2][m] -= Pt[rl * EPAD + p + L * m];
-        __syncthreads();
       }
+      tile_commit_corner(tr, Vl, invd);   // the next block's V (barriers inside)
     }
   }
 }
@@ -657,7 +717,7 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
   // Whole super-blocks of four full blocks, with 16 lanes per row and rulers
   // per row or per block, run as one launch each.
-  const bool sb_ok = wide && midg == 0 && B == BMAX && SB == SB_BLOCKS * BMAX &&
+  const bool sb_ok = wide && midg == 0 && B == BMAX && SB == SB_BLOCKS * BMAX && b.vec_u &&
                      (a.groupsize <= 0 || a.groupsize == BMAX);
   for (int64_t s1 = 0; s1 < c; s1 += SB) {
     const int64_t s2 = std::min(s1 + SB, c);
