@@ -44,7 +44,17 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the enumerations take int as their fixed underlying type, so every
+ * int a caller passes (from C, or a foreign-function interface) is a value of
+ * the type; the calls themselves reject values outside the lists.  In C an
+ * enumeration is an int already. */
+#ifdef __cplusplus
+#define GPTQ_ENUM_BASE : int
+#else
+#define GPTQ_ENUM_BASE
+#endif
+
+typedef enum GPTQ_ENUM_BASE {
   GPTQ_OK = 0,
   GPTQ_EINVAL = 1,        /* null pointer, negative size, bad enum value      */
   GPTQ_EDTYPE = 2,        /* dtype not supported by this call                 */
@@ -55,7 +65,7 @@ typedef enum {
   GPTQ_EHIP = 7           /* a HIP launch failed                               */
 } gptq_status;
 
-typedef enum { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
+typedef enum GPTQ_ENUM_BASE { GPTQ_F32 = 0, GPTQ_BF16 = 1, GPTQ_F16 = 2 } gptq_dtype;
 
 /* ------------------------------------------------------------------------
  * Hessian accumulation.  Page: "GPTQ, with the code open", section

@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 # slowest first: the pool starts them at once
 SOURCES = ["quantize.hip", "linear.hip", "gemm_f32.hip", "syrk.hip", "gemv.hip", "prepare.hip",
-           "hadamard.hip", "pack.hip", "gptq_api.hip"]
+           "hadamard.hip", "pack.hip", "gptq_api.hip", "workspace.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

@@ -41,6 +41,23 @@ constexpr int64_t kMaxGroups256 = ((int64_t(1) << 32) - 1) / 256;
 // Workgroups of 256 threads needed for n items at `per` items per workgroup.
 int64_t groups_for(int64_t n, int64_t per) { return (n + per - 1) / per; }
 
+// Bytes spanned by a rows x cols matrix with row stride ld (elements of
+// `elem` bytes), or -1 when that does not fit in 63 bits.
+int64_t extent_bytes(int64_t rows, int64_t ld, int64_t cols, int64_t elem) {
+  int64_t e = 0;
+  if (rows <= 0 || cols <= 0) return 0;
+  if (__builtin_mul_overflow(rows - 1, ld, &e) || __builtin_add_overflow(e, cols, &e) ||
+      __builtin_mul_overflow(e, elem, &e))
+    return -1;
+  return e;
+}
+
+// Whether [p, p + bytes) and [q, q + bytes_q) overlap (extents already known to fit).
+bool overlaps(const void* p, int64_t bytes, const void* q, int64_t bytes_q) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + (uint64_t)bytes_q && b < a + (uint64_t)bytes;
+}
+
 size_t elem_size(gptq_dtype t) { return t == GPTQ_F32 ? 4 : 2; }
 bool valid_dtype(int t) { return t == GPTQ_F32 || t == GPTQ_BF16 || t == GPTQ_F16; }
 
@@ -251,8 +268,8 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t r, int64_t c, int bits, cons
   if (bits != 3 && bits != 4) return fail(GPTQ_EUNSUPPORTED, fn, "packing supports 3 and 4 bits");
   if (bits == 4 && c % 8 != 0) return fail(GPTQ_ESHAPE, fn, "4-bit packing needs c % 8 == 0");
   if (bits == 3 && c % 32 != 0) return fail(GPTQ_ESHAPE, fn, "3-bit packing needs c % 32 == 0");
-  if (ld_words < c * bits / 32) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
   if (r > kMaxRows || c > (int64_t)INT_MAX) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
+  if (ld_words < (bits == 4 ? c / 8 : c / 32 * 3)) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
   // one thread per packed chunk (8 codes at 4 bits, 32 codes at 3 bits or with col_perm)
   if (groups_for(r * groups_for(c, (bits == 4 && !col_perm) ? 8 : 32), 256) > kMaxGroups256)
     return fail(GPTQ_EUNSUPPORTED, fn, "too many packed chunks for one launch");
@@ -283,7 +300,7 @@ gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t r, int64_t c, int 
   if (!y) return fail(GPTQ_EINVAL, fn, "y is NULL");
   if (!aligned(y, 4)) return fail(GPTQ_EALIGN, fn, "y misaligned");
   if (c > 0) {
-    if (ld_words < c * bits / 32) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
+    if (ld_words < c / 32 * bits) return fail(GPTQ_ESHAPE, fn, "ld_words < c * bits / 32");
     if (ld_groups < n_groups) return fail(GPTQ_ESHAPE, fn, "ld_groups < number of groups");
     if (!packed || !scales || !zeros || !x) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
     if (bits == 4 && (!aligned(packed, 16) || ld_words % 4 != 0))
@@ -312,18 +329,17 @@ gptq_status gptq_hadamard_rotate(const void* A, gptq_dtype at, int64_t rows, int
   if (d > 0 && d % block != 0) return fail(GPTQ_ESHAPE, fn, "block must divide d");
   if (rows == 0 || d == 0) return ok();
   if (lda < d || ldo < d) return fail(GPTQ_ESHAPE, fn, "lda and ldo must be >= d");
+  if (rows > kMaxRows || d > kMaxRows) return fail(GPTQ_EUNSUPPORTED, fn, "size too large");
   if ((rows * (d / block)) >= (int64_t)INT_MAX) return fail(GPTQ_EUNSUPPORTED, fn, "too many blocks");
   // one workgroup per tile of 4096 elements (8192 for b = 8192)
   if (groups_for(rows * (d / block), block == 8192 ? 1 : 4096 / block) > kMaxGroups256)
     return fail(GPTQ_EUNSUPPORTED, fn, "too many tiles for one launch");
   if (!A || !out) return fail(GPTQ_EINVAL, fn, "A or out is NULL");
   if (!aligned(A, elem_size(at)) || !aligned(out, elem_size(ot))) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
-  const char* a0 = static_cast<const char*>(A);
-  const char* a1 = a0 + ((rows - 1) * lda + d) * (int64_t)elem_size(at);
-  const char* o0 = static_cast<const char*>(out);
-  const char* o1 = o0 + ((rows - 1) * ldo + d) * (int64_t)elem_size(ot);
-  const bool overlap = a0 < o1 && o0 < a1;
-  if (overlap && !(A == out && at == ot && lda == ldo))
+  const int64_t ea = extent_bytes(rows, lda, d, (int64_t)elem_size(at));
+  const int64_t eo = extent_bytes(rows, ldo, d, (int64_t)elem_size(ot));
+  if (ea < 0 || eo < 0) return fail(GPTQ_EUNSUPPORTED, fn, "matrix extent exceeds 2^63 bytes");
+  if (overlaps(A, ea, out, eo) && !(A == out && at == ot && lda == ldo))
     return fail(GPTQ_EINVAL, fn, "out overlaps A (only exact in-place use is allowed)");
   gptq::launch_hadamard(A, (int)at, lda, rows, d, block, out, (int)ot, ldo, reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);
@@ -353,19 +369,14 @@ gptq_status gptq_linear_forward(const void* X, gptq_dtype xt, int64_t n_tok, int
   if (w16 && (ldx >= (int64_t(1) << 22) || ldw >= (int64_t(1) << 22)))
     return fail(GPTQ_EUNSUPPORTED, fn, "16-bit W_hat needs ldx and ldw below 2^22");
   if (!aligned(Y, elem_size(yt)) || (act == 1 && !aligned(G, 2))) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
-  const char* y0 = static_cast<const char*>(Y);
-  const char* y1 = y0 + ((n_tok - 1) * ldy + r) * (int64_t)elem_size(yt);
-  const char* x0 = static_cast<const char*>(X);
-  const char* x1 = x0 + ((n_tok - 1) * ldx + d) * 2;
-  const char* w0 = static_cast<const char*>(W_hat);
-  const char* w1 = w0 + ((r - 1) * ldw + d) * (int64_t)elem_size(wt);
-  if ((y0 < x1 && x0 < y1) || (y0 < w1 && w0 < y1)) return fail(GPTQ_EINVAL, fn, "Y overlaps X or W_hat");
-  if (act == 1) {
-    const char* g0 = static_cast<const char*>(G);
-    const char* g1 = g0 + ((n_tok - 1) * ldg + r) * 2;
-    if (y0 < g1 && g0 < y1 && !(Y == G && yt == xt && ldy == ldg))
-      return fail(GPTQ_EINVAL, fn, "Y overlaps G (only Y == G with the same type and stride is allowed)");
-  }
+  const int64_t ey = extent_bytes(n_tok, ldy, r, (int64_t)elem_size(yt));
+  const int64_t ex = extent_bytes(n_tok, ldx, d, 2);
+  const int64_t ew = extent_bytes(r, ldw, d, (int64_t)elem_size(wt));
+  const int64_t eg = act == 1 ? extent_bytes(n_tok, ldg, r, 2) : 0;
+  if (ey < 0 || ex < 0 || ew < 0 || eg < 0) return fail(GPTQ_EUNSUPPORTED, fn, "matrix extent exceeds 2^63 bytes");
+  if (overlaps(Y, ey, X, ex) || overlaps(Y, ey, W_hat, ew)) return fail(GPTQ_EINVAL, fn, "Y overlaps X or W_hat");
+  if (act == 1 && overlaps(Y, ey, G, eg) && !(Y == G && yt == xt && ldy == ldg))
+    return fail(GPTQ_EINVAL, fn, "Y overlaps G (only Y == G with the same type and stride is allowed)");
   gptq::launch_linear(X, (int)xt, n_tok, d, ldx, W_hat, w16, r, ldw, act, G, ldg, Y, (int)yt, ldy,
                       reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);
@@ -383,11 +394,9 @@ gptq_status gptq_round16(const float* src, int64_t rows, int64_t cols, int64_t l
   if (lds < cols || ldd < cols) return fail(GPTQ_ESHAPE, fn, "leading dimension too small");
   if (!src || !dst) return fail(GPTQ_EINVAL, fn, "a required pointer is NULL");
   if (!aligned(src, 4) || !aligned(dst, 2)) return fail(GPTQ_EALIGN, fn, "misaligned pointer");
-  const char* s0 = reinterpret_cast<const char*>(src);
-  const char* s1 = s0 + ((rows - 1) * lds + cols) * 4;
-  const char* d0 = static_cast<const char*>(dst);
-  const char* d1 = d0 + ((rows - 1) * ldd + cols) * 2;
-  if (s0 < d1 && d0 < s1) return fail(GPTQ_EINVAL, fn, "dst overlaps src");
+  const int64_t es = extent_bytes(rows, lds, cols, 4), ed = extent_bytes(rows, ldd, cols, 2);
+  if (es < 0 || ed < 0) return fail(GPTQ_EUNSUPPORTED, fn, "matrix extent exceeds 2^63 bytes");
+  if (overlaps(src, es, dst, ed)) return fail(GPTQ_EINVAL, fn, "dst overlaps src");
   gptq::launch_round16(src, rows, cols, lds, (int)dt, dst, ldd, reinterpret_cast<hipStream_t>(stream));
   return check_launch(fn);
 }

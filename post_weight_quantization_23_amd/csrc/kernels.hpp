@@ -46,6 +46,12 @@ void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t*
                     uint8_t* dead, int32_t* info, void* ws, hipStream_t s);
 
 // --- Quantization (quantize.hip) ---
+// Blocks per super-block: repairs inside it are applied as the loop goes,
+// repairs beyond it deferred to one product (quantize.hip).
+constexpr int64_t kSuperBlocks = 4;
+// The fp32 working copy of W (r x c) and the scaled errors of one
+// super-block (r x kSuperBlocks * blocksize), each 256-byte aligned
+// (workspace.hip).
 size_t quantize_workspace_bytes(int64_t r, int64_t c, int64_t blocksize);
 struct QuantArgs {
   const void* W;

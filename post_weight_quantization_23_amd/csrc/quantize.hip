@@ -510,7 +510,7 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
 // (16 float4 per thread, all in flight at once) and written to the one LDS
 // tile buffer when its phase comes, so the loads of the first update run
 // under the chain and each later load under the previous phase.
-constexpr int SB_BLOCKS = 4;
+constexpr int SB_BLOCKS = (int)kSuperBlocks;
 constexpr int EPAD = BMAX + 4;   // LDS row stride of the E and product tiles
 constexpr int TPAD = BMAX + 4;   // LDS row stride of a tile of U in an update (4 rows of an
                                  // MFMA operand read land on different banks)
@@ -637,12 +637,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-constexpr int64_t SUPER_BLOCKS = 4;
-
-size_t quantize_workspace_bytes(int64_t r, int64_t c, int64_t blocksize) {
-  const int64_t B = blocksize > 0 ? blocksize : 1;
-  return align256((size_t)r * c * sizeof(float)) + align256((size_t)SUPER_BLOCKS * B * r * sizeof(float));
-}
+constexpr int64_t SUPER_BLOCKS = kSuperBlocks;
 
 namespace {
 
