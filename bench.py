@@ -897,7 +897,7 @@ def main(argv=None) -> int:
         "hessian_tflops": hess_tflops,
         "stage_ms": {k: round(v, 4) for k, v in avg.items()},
         "roofline": {
-            "kernel": "gptq_hessian_accumulate: syrk16_kernel + reduce_partials_kernel (HIP events around the call)",
+            "kernel": "gptq_hessian_accumulate: syrk16_dma_kernel + reduce_partials_kernel (HIP events around the call)",
             "bound": "mfma",
             "achieved": hess_tflops,
             "peak": peak,
