@@ -55,22 +55,32 @@ __global__ __launch_bounds__(1024) void diag_dead_kernel(float* H, int64_t d, ui
 // reported through info) sorts as -inf so the ranks always form a permutation.
 GPTQ_DEV float sort_key(float v) { return __builtin_isnan(v) ? -__builtin_inff() : v; }
 
+// One workgroup per 64 columns i; its four waves count over the four
+// quarters of j and the partial counts are summed through LDS.  The scan
+// over j reads the same diag[j] in every lane of a wave (a broadcast).
 __global__ __launch_bounds__(256) void rank_kernel(const float* diag, int64_t d, int32_t* perm) {
-  __shared__ float tile[1024];
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ int64_t part[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
   const float di = i < d ? sort_key(diag[i]) : 0.f;
+  const int64_t q = (d + 3) / 4;
+  const int64_t j0 = wave * q, j1 = min(d, j0 + q);
   int64_t rank = 0;
-  for (int64_t base = 0; base < d; base += 1024) {
-    __syncthreads();
-    for (int k = threadIdx.x; k < 1024; k += 256) tile[k] = base + k < d ? sort_key(diag[base + k]) : 0.f;
-    __syncthreads();
-    const int lim = (int)min<int64_t>(1024, d - base);
-    for (int k = 0; k < lim; ++k) {
-      const float v = tile[k];
-      rank += (v > di) || (v == di && base + k < i);
-    }
+  int64_t j = j0;
+  for (; j + 8 <= j1; j += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = sort_key(diag[j + u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rank += (v[u] > di) || (v[u] == di && j + u < i);
   }
-  if (i < d) perm[rank] = (int32_t)i;
+  for (; j < j1; ++j) {
+    const float v = sort_key(diag[j]);
+    rank += (v > di) || (v == di && j < i);
+  }
+  part[wave][lane] = rank;
+  __syncthreads();
+  if (wave == 0 && i < d) perm[part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = (int32_t)i;
 }
 
 __global__ void identity_perm_kernel(int32_t* perm, int64_t d) {
@@ -447,7 +457,7 @@ void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t*
   hipLaunchKernelGGL(diag_dead_kernel, dim3(1), dim3(1024), 0, s, H, d, dead, info, diag);
   const unsigned gb = (unsigned)((d + 255) / 256);
   if (act_order) {
-    hipLaunchKernelGGL(rank_kernel, dim3(gb), dim3(256), 0, s, (const float*)diag, d, perm);
+    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((d + 63) / 64)), dim3(256), 0, s, (const float*)diag, d, perm);
     const unsigned gx = (unsigned)std::min<int64_t>((d + 255) / 256, 64);
     hipLaunchKernelGGL(permute_upper_kernel, dim3(gx, (unsigned)d), dim3(256), 0, s, (const float*)H, d,
                        (const int32_t*)perm, Wk);

@@ -563,8 +563,11 @@ __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1
   constexpr int L = 16, S = BMAX / L, ROWS = 16;
   __shared__ __attribute__((aligned(16))) float Vl[BMAX * TPAD];   // a block's V, or a tile of U
   __shared__ float invd[BMAX];
-  __shared__ float Et[ROWS * EPAD];   // scaled errors of the block just done
-  __shared__ float Pt[ROWS * EPAD];   // E_k U[k, k'] for one later block k'
+  // The scaled errors of the block just done, and then, once every thread
+  // holds its operands from them (the barrier after the first tile commit),
+  // the products E_k U[k, k'] for one later block k' at a time: one buffer.
+  __shared__ float Et[ROWS * EPAD];
+  float* const Pt = Et;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = tid % L, rl = tid / L;
