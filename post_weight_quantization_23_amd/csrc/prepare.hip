@@ -238,35 +238,87 @@ __device__ __forceinline__ void wave_gemm16(const float* A, int lda, const float
   __builtin_amdgcn_wave_barrier();
 }
 
-// C (n x m) = alpha * A * op(B) [+ C] on LDS arrays with the fp32 matrix
-// cores; n, m, K multiples of 32.  op(B) = B^T (B stored m x K) when bt, else
-// B (K x m).  32 x 32 output blocks are spread over the 4 waves; with
-// upper_only, blocks strictly below the diagonal are skipped.  Even and odd
-// K-pairs go to two accumulators, so consecutive MFMAs do not wait on each
-// other; the two are added at the end.
-__device__ __forceinline__ void lds_gemm(int n, int m, int K, const float* A, int lda, const float* B, int ldb, int bt,
-                         float* C, int ldc, float alpha, bool accumulate, bool upper_only) {
+// Which K-blocks (of the output block's edge) can hold non-zero products for
+// output block (bi, bj)
+// when one operand is triangular (its zeros below the diagonal are exact
+// zeros in LDS): KM_NONE all; KM_A_UPPER A upper (kb >= bi); KM_BT_UPPER
+// op(B) = B^T with B upper (kb >= bj); KM_B_UPPER op(B) = B upper (kb <= bj).
+enum { KM_NONE = 0, KM_A_UPPER = 1, KM_BT_UPPER = 2, KM_B_UPPER = 3 };
+
+GPTQ_DEV bool k_block_live(int km, int kb, int bi, int bj) {
+  if (km == KM_A_UPPER) return kb >= bi;
+  if (km == KM_BT_UPPER) return kb >= bj;
+  if (km == KM_B_UPPER) return kb <= bj;
+  return true;
+}
+
+// C (H x H) = alpha * A * op(B) [+ C] on LDS arrays, K = H, on the fp32
+// matrix cores.  op(B) = B^T (B stored H x K) when bt, else B (K x H).
+// K-blocks that a triangular operand zeroes are skipped, and with upper_only
+// blocks strictly below the diagonal are skipped.
+//   H = 64: 32 x 32 output blocks (v_mfma_f32_32x32x2f32), one per wave.
+//     Lane l supplies A[l % 32][k + l / 32] and B[k + l / 32][l % 32] and
+//     receives D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32] in accumulator v.
+//     Diagonal blocks are written whole (their entries below the diagonal
+//     are never read as U).
+//   H = 32: 16 x 16 output blocks (v_mfma_f32_16x16x4f32), one per wave, so
+//     all four waves work.  Lane l supplies A[l % 16][k + l / 16] and
+//     B[k + l / 16][l % 16] and receives D[4 (l / 16) + v][l % 16].  With
+//     upper_only only entries on and above the diagonal are written.
+// Even and odd K-steps go to two accumulators, so consecutive MFMAs do not
+// wait on each other.
+template <int H>
+__device__ __forceinline__ void lds_gemm(const float* A, int lda, const float* B, int ldb, int bt, float* C, int ldc,
+                                         float alpha, bool accumulate, bool upper_only, int km) {
+  constexpr int BS = H / 2, NBK = 2;   // output block edge; blocks per dimension
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nbm = m / 32, blocks = (n / 32) * nbm;
-  for (int blk = wave; blk < blocks; blk += 4) {
-    const int bi = blk / nbm, bj = blk % nbm;
-    if (upper_only && bj < bi) continue;
+  const int bi = wave / NBK, bj = wave % NBK;
+  if (upper_only && bj < bi) return;
+  if constexpr (H == 64) {
     floatx16 acc0, acc1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc0[v] = acc1[v] = 0.f;
-    const int r = 32 * bi + (lane & 31), c = 32 * bj + (lane & 31), kh = lane >> 5;
-#pragma unroll 8
-    for (int k = 0; k < K; k += 4) {
-      const float a0 = A[r * lda + k + kh], a1 = A[r * lda + k + 2 + kh];
-      const float b0 = bt ? B[c * ldb + k + kh] : B[(k + kh) * ldb + c];
-      const float b1 = bt ? B[c * ldb + k + 2 + kh] : B[(k + 2 + kh) * ldb + c];
-      acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc1, 0, 0, 0);
+    const int r = BS * bi + (lane & 31), c = BS * bj + (lane & 31), kh = lane >> 5;
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb) {
+      if (!k_block_live(km, kb, bi, bj)) continue;   // wave-uniform
+#pragma unroll
+      for (int k = BS * kb; k < BS * kb + BS; k += 4) {
+        const float a0 = A[r * lda + k + kh], a1 = A[r * lda + k + 2 + kh];
+        const float b0 = bt ? B[c * ldb + k + kh] : B[(k + kh) * ldb + c];
+        const float b1 = bt ? B[c * ldb + k + 2 + kh] : B[(k + 2 + kh) * ldb + c];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc1, 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int i = 32 * bi + 8 * (v >> 2) + 4 * kh + (v & 3);
+      const int i = BS * bi + 8 * (v >> 2) + 4 * kh + (v & 3);
       float* p = C + i * ldc + c;
+      const float sum = acc0[v] + acc1[v];
+      *p = accumulate ? __builtin_fmaf(alpha, sum, *p) : alpha * sum;
+    }
+  } else {
+    static_assert(H == 32, "the leaf's products are 64 or 32 wide");
+    floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const int r = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int kb = 0; kb < NBK; ++kb) {
+      if (!k_block_live(km, kb, bi, bj)) continue;   // wave-uniform
+#pragma unroll
+      for (int s4 = 0; s4 < BS / 4; ++s4) {
+        const int k = BS * kb + 4 * s4 + kq;
+        const float a = A[(BS * bi + r) * lda + k];
+        const float b = bt ? B[(BS * bj + r) * ldb + k] : B[k * ldb + BS * bj + r];
+        if (s4 & 1) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc1, 0, 0, 0);
+        else acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = BS * bi + 4 * kq + v, j = BS * bj + r;
+      if (upper_only && j < i) continue;
+      float* p = C + i * ldc + j;
       const float sum = acc0[v] + acc1[v];
       *p = accumulate ? __builtin_fmaf(alpha, sum, *p) : alpha * sum;
     }
@@ -317,14 +369,14 @@ __device__ __forceinline__ void leaf_rec(float* M, int o, const LeafScratch& ts,
     float* U22 = M + o2 * LDM + o2;
     float* U11 = M + o * LDM + o;
     leaf_rec<h>(M, o2, ts, info, gbase, pad);
-    lds_gemm(h, h, h, Bm, LDM, U22, LDM, 1, T1, ldt, 1.f, false, false);    // T1 = B U22^T
+    lds_gemm<h>(Bm, LDM, U22, LDM, 1, T1, ldt, 1.f, false, false, KM_BT_UPPER);   // T1 = B U22^T
     __syncthreads();
-    lds_gemm(h, h, h, T1, ldt, T1, ldt, 1, U11, LDM, -1.f, true, true);     // A -= T1 T1^T
+    lds_gemm<h>(T1, ldt, T1, ldt, 1, U11, LDM, -1.f, true, true, KM_NONE);        // A -= T1 T1^T
     __syncthreads();
     leaf_rec<h>(M, o, ts, info, gbase, pad);
-    lds_gemm(h, h, h, U11, LDM, T1, ldt, 0, T2, ldt, 1.f, false, false);    // T2 = U11 T1
+    lds_gemm<h>(U11, LDM, T1, ldt, 0, T2, ldt, 1.f, false, false, KM_A_UPPER);    // T2 = U11 T1
     __syncthreads();
-    lds_gemm(h, h, h, T2, ldt, U22, LDM, 0, Bm, LDM, -1.f, false, false);   // U12 = -T2 U22
+    lds_gemm<h>(T2, ldt, U22, LDM, 0, Bm, LDM, -1.f, false, false, KM_B_UPPER);   // U12 = -T2 U22
     __syncthreads();
   }
 }
