@@ -70,19 +70,83 @@ GPTQ_DEV float load_w(const void* W, int wt, int64_t idx) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// Eight consecutive weights of a row as fp32 (16-byte aligned, 16-bit types:
+// one 16-byte load; fp32: two).
+GPTQ_DEV void load_w8(const void* W, int wt, int64_t idx, float (&v)[8]) {
+  if (wt == 0) {
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(W) + idx);
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(W) + idx + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = lo[e];
+      v[4 + e] = hi[e];
+    }
+    return;
+  }
+  const uint4 q = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(W) + idx);
+  const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint16_t h0 = (uint16_t)(w4[e] & 0xFFFFu), h1 = (uint16_t)(w4[e] >> 16);
+    if (wt == 1) {
+      v[2 * e] = __uint_as_float((uint32_t)h0 << 16);
+      v[2 * e + 1] = __uint_as_float((uint32_t)h1 << 16);
+    } else {
+      v[2 * e] = (float)__builtin_bit_cast(_Float16, h0);
+      v[2 * e + 1] = (float)__builtin_bit_cast(_Float16, h1);
+    }
+  }
+}
+
 // One workgroup per row: gather/cast into processing order, zero dead inputs,
-// per-row ruler on the original row.
+// per-row ruler on the original row.  MODE 0: one weight per thread and step.
+// MODE 1 (no permutation, c % 8 == 0, rows of W 16-byte aligned) and MODE 2
+// (a permutation 16-byte aligned, c % 8 == 0): eight consecutive processing
+// columns per thread and step, stored with 16-byte stores; MODE 1 reads W
+// with 16-byte loads, MODE 2 reads the permutation with 16-byte loads and
+// gathers the eight weights independently.
+template <int MODE>
 __global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp) {
   const int64_t row = blockIdx.x;
   const int64_t c = a.c;
   float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int64_t k = threadIdx.x; k < c; k += 256) {
-    const int64_t src = a.perm ? clamp_col(a.perm[k], c) : k;
-    const float v = load_w(a.W, a.wt, row * a.ldw + src);
-    mn = fminf(mn, v);
-    mx = fmaxf(mx, v);
-    const bool dk = a.dead && a.dead[src];
-    Wp[row * c + k] = dk ? 0.f : v;
+  if constexpr (MODE != 0) {
+    for (int64_t k = 8 * (int64_t)threadIdx.x; k < c; k += 8 * 256) {
+      float v[8];
+      int64_t src[8];
+      if constexpr (MODE == 1) {
+        load_w8(a.W, a.wt, row * a.ldw + k, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) src[e] = k + e;
+      } else {
+        const int4 p0 = *reinterpret_cast<const int4*>(a.perm + k);
+        const int4 p1 = *reinterpret_cast<const int4*>(a.perm + k + 4);
+        const int32_t pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          src[e] = clamp_col(pr[e], c);
+          v[e] = load_w(a.W, a.wt, row * a.ldw + src[e]);
+        }
+      }
+      floatx4 o[2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mn = fminf(mn, v[e]);
+        mx = fmaxf(mx, v[e]);
+        o[e >> 2][e & 3] = (a.dead && a.dead[src[e]]) ? 0.f : v[e];
+      }
+      *reinterpret_cast<floatx4*>(Wp + row * c + k) = o[0];
+      *reinterpret_cast<floatx4*>(Wp + row * c + k + 4) = o[1];
+    }
+  } else {
+    for (int64_t k = threadIdx.x; k < c; k += 256) {
+      const int64_t src = a.perm ? clamp_col(a.perm[k], c) : k;
+      const float v = load_w(a.W, a.wt, row * a.ldw + src);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+      const bool dk = a.dead && a.dead[src];
+      Wp[row * c + k] = dk ? 0.f : v;
+    }
   }
   if (a.groupsize <= 0) {
     __shared__ float smn[256], smx[256];
@@ -495,7 +559,8 @@ __global__ __launch_bounds__(256) void block_kernel(BlockArgs a) {
 }
 
 // A super-block of SB_BLOCKS full blocks in one launch (16 lanes per row, 16
-// rows per workgroup, groups of one block or one ruler per row): the row's
+// rows per workgroup; one ruler per row, groups of one block, or with MIDG ==
+// 32 groups of 32 or 64 columns, which start and end inside a block): the row's
 // 512 columns stay in registers from the first block to the last.  After
 // each block, its scaled errors E (16 rows x 128, through LDS) update the
 // super-block's later blocks on the matrix cores,
@@ -559,6 +624,7 @@ GPTQ_DEV void tile_commit_corner(const TileRegs& t, float* Vl, float* invd) {
   __syncthreads();
 }
 
+template <int MIDG>
 __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1) {
   constexpr int L = 16, S = BMAX / L, ROWS = 16;
   __shared__ __attribute__((aligned(16))) float Vl[BMAX * TPAD];   // a block's V, or a tile of U
@@ -597,7 +663,7 @@ __global__ __launch_bounds__(256) void superblock_kernel(BlockArgs a, int64_t s1
     float w[S], ereg[S];
 #pragma unroll
     for (int m = 0; m < S; ++m) w[m] = wsb[kb][m];
-    block_columns<16, 0, true>(b, Vl, invd, p, row, valid, Wrow, w, wsb[kb], ereg);
+    block_columns<16, MIDG, true>(b, Vl, invd, p, row, valid, Wrow, w, wsb[kb], ereg);
     if (kb + 1 < SB_BLOCKS) {
 #pragma unroll
       for (int m = 0; m < S; ++m) Et[rl * EPAD + p + L * m] = ereg[m];   // 0 on rows past r
@@ -686,7 +752,13 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   float* Wp = reinterpret_cast<float*>(a.ws);
   // E: r x SB row-major, the scaled errors of the current super-block
   float* E = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + align256((size_t)r * c * sizeof(float)));
-  hipLaunchKernelGGL(init_kernel, dim3((unsigned)r), dim3(256), 0, s, a, Wp);
+  const int wbytes = a.wt == 0 ? 4 : 2;
+  const bool vec_w = a.perm == nullptr && c % 8 == 0 && (reinterpret_cast<uintptr_t>(a.W) & 15) == 0 &&
+                     (a.ldw * wbytes) % 16 == 0;
+  const bool vec_p = a.perm != nullptr && c % 8 == 0 && (reinterpret_cast<uintptr_t>(a.perm) & 15) == 0;
+  if (vec_w) hipLaunchKernelGGL((init_kernel<1>), dim3((unsigned)r), dim3(256), 0, s, a, Wp);
+  else if (vec_p) hipLaunchKernelGGL((init_kernel<2>), dim3((unsigned)r), dim3(256), 0, s, a, Wp);
+  else hipLaunchKernelGGL((init_kernel<0>), dim3((unsigned)r), dim3(256), 0, s, a, Wp);
   hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, s, a.perm, c,
                      a.groupsize, a.g_idx);
   BlockArgs b;
@@ -715,15 +787,18 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   const dim3 g16((unsigned)((r + 15) / 16)), g4((unsigned)((r + 63) / 64));
   // Whole super-blocks of four full blocks, with 16 lanes per row and rulers
   // per row or per block, run as one launch each.
-  const bool sb_ok = wide && midg == 0 && B == BMAX && SB == SB_BLOCKS * BMAX && b.vec_u &&
-                     (a.groupsize <= 0 || a.groupsize == BMAX);
+  // Groups of 32 or 64 lie inside a block, so their rulers are fitted from
+  // the registers of the block at hand (MIDG == 32).
+  const bool sb_ok = wide && B == BMAX && SB == SB_BLOCKS * BMAX && b.vec_u &&
+                     (a.groupsize <= 0 || a.groupsize == BMAX || a.groupsize == 32 || a.groupsize == 64);
   for (int64_t s1 = 0; s1 < c; s1 += SB) {
     const int64_t s2 = std::min(s1 + SB, c);
     if (sb_ok && s2 - s1 == SB) {
       b.i1 = s1;
       b.Bw = BMAX;
       b.E = E;
-      hipLaunchKernelGGL(superblock_kernel, g16, dim3(256), 0, s, b, s1);
+      if (midg == 32) hipLaunchKernelGGL((superblock_kernel<32>), g16, dim3(256), 0, s, b, s1);
+      else hipLaunchKernelGGL((superblock_kernel<0>), g16, dim3(256), 0, s, b, s1);
       if (s2 < c) gemm_update(s, r, c, E, SB, (int)(s2 - s1), a.U, s1, s2, c, Wp);
       continue;
     }

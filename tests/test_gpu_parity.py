@@ -258,6 +258,8 @@ CASES = [
     (1030, 1100, 4, 128, 128, True, 2, "bfloat16"),  # several super-blocks, ragged tail
     (1024, 1536, 3, -1, 128, False, 1, "float16"),   # one ruler per row, three whole super-blocks
     (70, 1300, 3, 256, 64, False, 0, "float16"),     # groups of 4 blocks across super-blocks
+    (1040, 1100, 4, 32, 128, False, 1, "bfloat16"),  # whole super-blocks with groups of 32, ragged tail
+    (1100, 1024, 3, 64, 128, True, 0, "float16"),    # whole super-blocks with groups of 64, act-order
 ]
 
 
@@ -279,6 +281,7 @@ SYM_CASES = [
     (40, 160, 8, 64, 64, False, 0, "float16"),
     (50, 256, 2, -1, 128, True, 2, "float32"),
     (20, 300, 4, 256, 128, False, 0, "float32"),     # group spanning two blocks
+    (1030, 1024, 4, 32, 128, False, 0, "bfloat16"),  # whole super-blocks with groups of 32
 ]
 
 
@@ -351,6 +354,40 @@ def test_repeat_runs_are_bitwise_identical():
         outs.append((torch.triu(H).cpu(), U.cpu(), o["codes"].cpu(), o["scales"].cpu(), o["row_loss"].cpu()))
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("wdtype", ["bfloat16", "float32"])
+def test_weight_cast_paths_agree(wdtype):
+    """The three ways the quantizer reads W into its working copy -- no
+    permutation with 16-byte aligned rows (eight weights per load), a
+    16-byte aligned permutation (eight gathered weights per thread), and
+    anything else (one weight per thread: unaligned rows without a
+    permutation, or an unaligned permutation) -- give the same bits."""
+    q = gq()
+    r, c = 1030, 1024
+    dt = torch.bfloat16 if wdtype == "bfloat16" else torch.float32
+    W = to_dev(S.weights_host(r, c, wid=95, dtype=wdtype), dt)
+    X = S.activations_host(3 * c, c, "t4", outliers=4, gain=20.0, wid=96)
+    X[:, [5, 700]] = 0.0                                     # two dead inputs
+    H = gpu_hessian(X, "float32")
+    U = H.clone()
+    perm, dead, _ = q.prepare(U, 0.01, False)
+    assert int(dead.sum()) == 2
+    Wbig = torch.zeros((r, c + 1), dtype=dt, device="cuda")
+    Wbig[:, 1:] = W
+    W_un = Wbig[:, 1:]                                       # rows at an odd element offset
+    pbig = torch.zeros(c + 1, dtype=torch.int32, device="cuda")
+    pbig[1:] = perm
+    perm_un = pbig[1:]                                       # 4 bytes past a 16-byte boundary
+    assert W_un.data_ptr() % 16 != 0 and perm_un.data_ptr() % 16 != 0
+    outs = [q.quantize_layer(W, U, None, dead, bits=4, groupsize=128, want_w_hat=True),
+            q.quantize_layer(W, U, perm, dead, bits=4, groupsize=128, want_w_hat=True),
+            q.quantize_layer(W_un, U, None, dead, bits=4, groupsize=128, want_w_hat=True),
+            q.quantize_layer(W, U, perm_un, dead, bits=4, groupsize=128, want_w_hat=True)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for k in ("codes", "scales", "zeros", "g_idx", "w_hat", "row_loss"):
+            assert torch.equal(outs[0][k], o[k]), k
 
 
 def test_empty_inputs_are_no_ops():
