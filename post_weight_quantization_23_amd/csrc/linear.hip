@@ -13,8 +13,9 @@
 //
 // Layout and tiling: X token-major [n_tok, d] and W_hat [r, d] are both
 // contiguous along the contraction axis, so no transpose is needed: a
-// workgroup of 4 waves computes a 256 x 256 tile (each wave 128 x 128 as
-// 4 x 4 v_mfma_f32_32x32x16 blocks, accumulators in AGPRs) over K-steps of
+// workgroup computes a 256 x 256 tile (8 waves of 128 x 64 as 4 x 2
+// v_mfma_f32_32x32x16 blocks when the weights are already 16-bit, else 4
+// waves of 128 x 128 as 4 x 4 blocks, accumulators in AGPRs) over K-steps of
 // 64, with each 16-byte run of 8 K-values written to an LDS row of 128 bytes
 // whose chunks are XOR-swizzled by the row (conflict-free MFMA operand reads).
 // Two ways in for W_hat.  Given as fp32 (the quantizer's output), it is read
@@ -158,19 +159,22 @@ GPTQ_DEV void lin_tile(int b, int ntm, int ntn, int64_t& tm, int& tn) {
 // of its row, so chunk c of row f lands at position c ^ lswz(f), where the
 // operand reads expect it.  Rows past the end of X or W fall outside the
 // descriptors' records and load zeros.
-template <int DT>
+// NQ: load instructions per wave and operand (8 rows each; 32 per operand
+// and step over the workgroup's waves); NB: 32-column MFMA blocks per wave.
+template <int DT, int NQ, int NB>
 GPTQ_DEV void lin_steps_dma(const LinArgs& a, int64_t m0, int n0, int wm, int wn, unsigned char* smem,
-                            floatx16 (&acc)[4][4]) {
+                            floatx16 (&acc)[4][NB]) {
   constexpr int SLAB = LT * LROWB, BUF = 2 * SLAB;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   lds_u8* lbase = (lds_u8*)smem;  // generic to LDS address space
   const int nsteps = a.K / LK;
   // byte offsets of the lane's chunks inside a K-step (ldx, ldw < 2^22)
-  int offx[8], offw[8];
+  static_assert(NQ <= 8, "at most 8 load instructions per wave");
+  int offx[8], offw[8];   // the first NQ are used
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = 8 * (wave * 8 + q) + (lane >> 3), c = (lane & 7) ^ lswz(row);
+  for (int q = 0; q < NQ; ++q) {
+    const int row = 8 * (wave * NQ + q) + (lane >> 3), c = (lane & 7) ^ lswz(row);
     offx[q] = row * (int)a.ldx * 2 + 16 * c;
     offw[q] = row * (int)a.ldw * 2 + 16 * c;
   }
@@ -183,14 +187,14 @@ GPTQ_DEV void lin_steps_dma(const LinArgs& a, int64_t m0, int n0, int wm, int wn
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.W16 + (int64_t)n0 * a.ldw + k0), (short)0, (int)(wrec - 2 * k0), 0x00020000);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int I = wave * 8 + q;
+    for (int q = 0; q < NQ; ++q) {
+      const int I = wave * NQ + q;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, lbase + b * BUF + I * 1024, 16, offx[q], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lbase + b * BUF + SLAB + I * 1024, 16, offw[q], 0, 0, 0);
     }
   };
-  u32x4 fa[2][4], fb[2][4];
-  auto frags = [&](const unsigned char* as, const unsigned char* bs, int kk, u32x4 (&xa)[4], u32x4 (&xb)[4]) {
+  u32x4 fa[2][4], fb[2][NB];
+  auto frags = [&](const unsigned char* as, const unsigned char* bs, int kk, u32x4 (&xa)[4], u32x4 (&xb)[NB]) {
     const int chunk = 2 * kk + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -198,16 +202,16 @@ GPTQ_DEV void lin_steps_dma(const LinArgs& a, int64_t m0, int n0, int wm, int wn
       xa[i] = *reinterpret_cast<const u32x4*>(as + f * LROWB + ((chunk ^ lswz(f)) * 16));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int f = wn + 32 * j + (lane & 31);
       xb[j] = *reinterpret_cast<const u32x4*>(bs + f * LROWB + ((chunk ^ lswz(f)) * 16));
     }
   };
-  auto mfmas = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[4]) {
+  auto mfmas = [&](const u32x4 (&xa)[4], const u32x4 (&xb)[NB]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = lmfma<DT>(xa[i], xb[j], acc[i][j]);
+      for (int j = 0; j < NB; ++j) acc[i][j] = lmfma<DT>(xa[i], xb[j], acc[i][j]);
   };
   dma(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -327,9 +331,18 @@ GPTQ_DEV void lin_steps_f32(const LinArgs& a, int64_t m0, int n0, int wm, int wn
 
 // Template arguments: activation type (1 bf16, 2 f16), epilogue (0 plain,
 // 1 gated), output type (0 f32, 1 bf16, 2 f16), weights already 16-bit.
+// With 16-bit weights the workgroup is 8 waves of 128 x 64 (two per SIMD, so
+// one wave's operand reads overlap the other's MFMAs); with fp32 weights 4
+// waves of 128 x 128 (the register staging needs the registers).
 template <int DT, int ACT, int YT, bool W16>
-__global__ __launch_bounds__(256, 1) void linear_kernel(LinArgs a) {
+__global__ __launch_bounds__(W16 ? 512 : 256, 1) void linear_kernel(LinArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lsm[];
+  constexpr int NW = W16 ? 8 : 4;        // waves
+  constexpr int NB = W16 ? 2 : 4;        // 32-column MFMA blocks per wave
+  constexpr int WN = 32 * NB;            // columns per wave
+  constexpr int LPR = 8 * NB;            // epilogue lanes per row (4 columns each)
+  constexpr int RPP = 64 / LPR;          // epilogue rows per pass
+  constexpr int PASSES = 32 / RPP;       // passes per 32-row strip
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t tm;
@@ -337,36 +350,36 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(LinArgs a) {
   lin_tile((int)blockIdx.x, a.ntm, a.ntn, tm, tn);
   const int64_t m0 = tm * LT;
   const int n0 = tn * LT;
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int wm = (wave / (NW / 2)) * 128, wn = (wave % (NW / 2)) * WN;
 
-  floatx16 acc[4][4];
+  floatx16 acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  if constexpr (W16) lin_steps_dma<DT>(a, m0, n0, wm, wn, lsm, acc);
+  if constexpr (W16) lin_steps_dma<DT, 32 / NW, NB>(a, m0, n0, wm, wn, lsm, acc);
   else lin_steps_f32<DT>(a, m0, n0, wm, wn, lsm, acc);
 
-  // Epilogue through LDS, one 32-row strip of each wave's 128 x 128 block at a
-  // time (16 KiB per wave): the accumulators are written with static indices
-  // (lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each 32 x 32
-  // block), then read back four consecutive columns at a time: lane l takes
-  // columns 4 (l % 32) .. +3 of rows 2k + l / 32, k = 0 .. 15, so each row is
-  // written by 32 lanes in one contiguous run.  In the gated mode the gate
-  // values of strip i+1 (16 eight-byte loads per lane) are requested before
-  // strip i is processed, and those of strip 0 before the first barrier.
-  float* ep = reinterpret_cast<float*>(lsm) + wave * (32 * 128);
-  const int cq = lane & 31, rh = lane >> 5;
+  // Epilogue through LDS, one 32-row strip of each wave's 128 x WN block at a
+  // time (32 x WN floats per wave): the accumulators are written with static
+  // indices (lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] of each
+  // 32 x 32 block), then read back four consecutive columns at a time: lane l
+  // takes columns 4 (l % LPR) .. +3 of rows RPP k + l / LPR, so each row is
+  // written by LPR lanes in one contiguous run.  In the gated mode the gate
+  // values of strip i+1 (eight-byte loads) are requested before strip i is
+  // processed, and those of strip 0 before the first barrier.
+  float* ep = reinterpret_cast<float*>(lsm) + wave * (32 * WN);
+  const int cq = lane % LPR, rh = lane / LPR;
   const int gn = n0 + wn + 4 * cq;
   const bool full4 = gn + 4 <= a.N;
-  uint2 gq[2][16];
-  auto load_gate = [&](int i, uint2 (&g)[16]) __attribute__((always_inline)) {
+  uint2 gq[2][PASSES];
+  auto load_gate = [&](int i, uint2 (&g)[PASSES]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int64_t gm = m0 + wm + 32 * i + 2 * k + rh;
+    for (int k = 0; k < PASSES; ++k) {
+      const int64_t gm = m0 + wm + 32 * i + RPP * k + rh;
       const uint16_t* gp = a.G + gm * a.ldg + gn;
       if (gm < a.M && full4 && a.gvec) {
         g[k] = *reinterpret_cast<const uint2*>(gp);
@@ -386,16 +399,16 @@ __global__ __launch_bounds__(256, 1) void linear_kernel(LinArgs a) {
     if constexpr (ACT == 1 && i + 1 < 4) load_gate(i + 1, gq[(i + 1) & 1]);
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        ep[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * 128 + 32 * j + (lane & 31)] = acc[i][j][v];
+        ep[(8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * WN + 32 * j + (lane & 31)] = acc[i][j][v];
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int r = 2 * k + rh;
+    for (int k = 0; k < PASSES; ++k) {
+      const int r = RPP * k + rh;
       const int64_t gm = m0 + wm + 32 * i + r;
-      const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * 128 + 4 * cq);
+      const floatx4 v = *reinterpret_cast<const floatx4*>(ep + r * WN + 4 * cq);
       float g[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (ACT == 1) {
         const uint2 w = gq[i & 1][k];
@@ -502,7 +515,7 @@ void launch_linear(const void* X, int xt, int64_t n_tok, int64_t d, int64_t ldx,
       return true;                                                                                    \
     }();                                                                                              \
     (void)set;                                                                                        \
-    hipLaunchKernelGGL((linear_kernel<D_, A_, Y_, W_>), grid, dim3(256), lds, s, a);                 \
+    hipLaunchKernelGGL((linear_kernel<D_, A_, Y_, W_>), grid, dim3((W_) ? 512 : 256), lds, s, a);    \
   } while (0)
 #define GPTQ_LIN_W(D_, A_, Y_)                  \
   do {                                          \
