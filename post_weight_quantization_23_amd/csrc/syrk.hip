@@ -493,15 +493,21 @@ SyrkPlan plan_syrk(int64_t d, int64_t n_tok) {
   p.tiles = nt * (nt + 1) / 2;
   const int64_t steps = (n_tok + KSTEP - 1) / KSTEP;
   // Enough workgroups to cover the 256 CUs evenly, each with >= 16 K-steps.
+  // Each split adds a round trip of partial tiles through memory: a small
+  // charge per split while the tiles are few (the partials are small next to
+  // the work), a larger one from 1024 tiles on, and at most 16384 partial
+  // tiles (4 GiB) in all.
   int best = 1;
-  if (p.tiles < 1024) {
+  if (p.tiles < 4096) {
     double best_eff = -1.0;
+    const double per_split = p.tiles < 1024 ? 0.002 : 0.01;
     for (int s = 1; s <= 64; ++s) {
       if (s > 1 && steps / s < 16) break;
+      if (s > 1 && (int64_t)p.tiles * s > 16384) break;
       const int64_t wgs = (int64_t)p.tiles * s;
       const int64_t waves = (wgs + 255) / 256;
       const double eff = (double)wgs / (double)(waves * 256);
-      const double score = eff - (wgs < 512 ? 0.5 : 0.0) - 0.002 * s;
+      const double score = eff - (wgs < 512 ? 0.5 : 0.0) - per_split * s;
       if (score > best_eff) {
         best_eff = score;
         best = s;
