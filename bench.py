@@ -907,6 +907,24 @@ def main(argv=None) -> int:
             "algorithmic_flops_per_launch": flops_h,
         },
     }
+    # The other stages against their own bounds, from the same HIP events (a
+    # stage's time includes all of its kernels, so these are lower bounds of
+    # the rate of its dominant kernel): the factor's 2d^3/3 flops and the
+    # lazy updates' r*c*(c - blocksize) flops against the fp32 matrix-core
+    # peak, the pack's (1 + bits/8) bytes per weight against HBM.
+    f_prep = 2.0 * d ** 3 / 3.0
+    f_lazy = float(r) * c * max(c - w.blocksize, 0)
+    b_pack = r * c * (1.0 + w.bits / 8.0)
+    rec["stage_roofline"] = {
+        "prepare": {"bound": "mfma", "achieved": f_prep / (avg["prepare"] / 1e3) / 1e12, "peak": PEAK_FP32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": f_prep / (avg["prepare"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
+                    "algorithmic_flops": f_prep},
+        "quantize": {"bound": "mfma", "achieved": f_lazy / (avg["quantize"] / 1e3) / 1e12, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": f_lazy / (avg["quantize"] / 1e3) / 1e12 / PEAK_FP32_TFLOPS,
+                     "algorithmic_flops": f_lazy, "note": "lazy-update flops over the whole call (chain included)"},
+        "pack": {"bound": "hbm", "achieved": b_pack / (avg["pack"] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": b_pack / (avg["pack"] / 1e3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": b_pack},
+    }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(W, X, w)
