@@ -14,7 +14,7 @@ oracle timed on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
     python bench.py --copy-probe      # plain copy of known size (PMC calibration)
-    python bench.py --gemv [--gemv-model llama7b|opt175b] [--steps K] [--warmup W]
+    python bench.py --gemv [--gemv-model llama7b|opt175b] [--fused-inputs] [--steps K] [--warmup W]
     python bench.py --hadamard [--workload NAME] [--steps K] [--warmup W]
     python bench.py --stack [--blocks B] [--steps K] [--warmup W]
     python bench.py --sweep [--sweep-blocks 32] [--rotate]
@@ -149,6 +149,15 @@ GEMV_MODELS = {
 }
 
 
+# The same models with the projections that read one input stored as one
+# matrix (rows concatenated): q, k and v; gate and up (Llama); fc1 alone and
+# q, k, v (OPT).  One launch then serves what were two or three.
+GEMV_FUSED = {
+    "llama7b": [("qkv", 3 * 4096, 4096), ("o", 4096, 4096), ("gate_up", 2 * 11008, 4096), ("down", 4096, 11008)],
+    "opt175b": [("qkv", 3 * 12288, 12288), ("out", 12288, 12288), ("fc1", 49152, 12288), ("fc2", 12288, 49152)],
+}
+
+
 def gemv_bytes(r: int, c: int, bits: int, groupsize: int, xbytes: int = 2) -> int:
     """Algorithmic HBM bytes of one launch: packed words, fp32 scales and int32
     zeros (one per row and group), x once, y once."""
@@ -203,6 +212,9 @@ def bench_gemv(args) -> int:
     from synth import inputs as S
 
     blocks, shapes, bits, gs, xdt = GEMV_MODELS[args.gemv_model]
+    if args.fused_inputs:
+        shapes = GEMV_FUSED[args.gemv_model]
+    tag = f"{args.gemv_model}_decode_token_{bits}bit_g{gs}" + ("_fused_inputs" if args.fused_inputs else "")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     xdtype = getattr(torch, xdt)
@@ -314,7 +326,8 @@ def bench_gemv(args) -> int:
 
     rec = {
         "metric": f"dequantizing GEMV, one generated token (batch 1) through {args.gemv_model}'s "
-                  f"{len(layers)} linear layers, {bits}-bit g{gs}: weights/s",
+                  f"{len(layers)} linear " + ("launches (projections of one input stored as one matrix)"
+                                              if args.fused_inputs else "layers") + f", {bits}-bit g{gs}: weights/s",
         "value": total_w / (ms_tok * 1e-3),
         "unit": "weights/s",
         "n_gpus": 1,
@@ -327,8 +340,8 @@ def bench_gemv(args) -> int:
         "dtype": "f16 dot (codes x activations), f32 sums",
         "data": "synthetic (seeded random packed words, log-normal scales, uniform zero points, "
                 "Student-t(4) activations with outlier channels)",
-        "config": {"workload": f"{args.gemv_model}_decode_token_{bits}bit_g{gs}", "layers": len(layers),
-                   "weights": total_w, "bytes_per_token": total_b, "x_dtype": xdt},
+        "config": {"workload": tag, "layers": len(layers), "weights": total_w, "bytes_per_token": total_b,
+                   "x_dtype": xdt, "fused_inputs": bool(args.fused_inputs)},
         "effective_GBps": total_b / (ms_tok * 1e-3) / 1e9,
         "ms_per_token_eager_launches": ms_eager,
         "roofline": {
@@ -340,7 +353,7 @@ def bench_gemv(args) -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": load_traffic(f"{args.gemv_model}_decode_token_{bits}bit_g{gs}", GEMV_TRAFFIC_FILE, GEMV_SOURCE),
+            "traffic": load_traffic(tag, GEMV_TRAFFIC_FILE, GEMV_SOURCE),
             "algorithmic_bytes_per_launch": b_launch,
             "us_per_launch": us_launch,
         },
@@ -768,6 +781,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--gemv", action="store_true")
     ap.add_argument("--gemv-model", default="llama7b", choices=sorted(GEMV_MODELS))
+    ap.add_argument("--fused-inputs", action="store_true",
+                    help="--gemv: projections that read one input stored as one matrix (q|k|v, gate|up)")
     ap.add_argument("--hadamard", action="store_true")
     ap.add_argument("--stack", action="store_true")
     ap.add_argument("--grid", action="store_true")
