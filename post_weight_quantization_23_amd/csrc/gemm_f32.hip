@@ -268,11 +268,13 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // LDS tiles are plain copies of the operand rows as they lie in memory --
 // A[m][k] rows (a_trans == 0) or A^T [k][m] rows, B[k][n] rows (b_trans == 0)
 // or B^T [n][k] rows -- and each MFMA operand is read with the matching
-// strides.  Masked (triangular) elements and k >= K are replaced by zero as
-// they are read, whatever LDS holds; rows past the end of an operand load
-// zeros from the descriptor bounds, and columns past M or N only reach
-// outputs that are not stored.  The operands and their order are those of
-// gemm_f32_kernel, so both kernels give the same bits.
+// strides.  On the K-steps that cross a triangle's diagonal or the end of K
+// the workgroup first overwrites the masked elements (and those with
+// k >= K) of the landed tiles with zeros in LDS; the MFMA loop itself has a
+// single body, so the accumulators stay in the AGPRs across steps.  Rows past
+// the end of an operand load zeros from the descriptor bounds, and columns
+// past M or N only reach outputs that are not stored.  The operands and their
+// order are those of gemm_f32_kernel, so both kernels give the same bits.
 GPTQ_DEV int kswz(int r) { return (r >> 1) & 7; }
 
 // The K-loop of gemm_f32_dma_kernel (a device function, so that the
@@ -337,51 +339,68 @@ GPTQ_DEV void gemm_steps_dma(const GemmArgs& g, int m0, int n0, int k_lo, int k_
       const float* as = gemm_smem + buf * (BUF / 4);
       const float* bs = as + ABYTES / 4;
       // Masks and the K tail only matter on steps that cross a triangle's
-      // diagonal or the end of K (a uniform test); other steps read plainly.
+      // diagonal or the end of K (a uniform test); those steps zero the
+      // masked elements of this buffer first, the others read plainly.
       bool plain = k0 + KT <= g.K;
       if (g.a_mask == MASK_UPPER) plain = plain && k0 + g.a_off >= m0 + TM - 1;
       if (g.a_mask == MASK_LOWER) plain = plain && m0 + g.a_off >= k0 + KT - 1;
       if (g.b_mask == MASK_UPPER) plain = plain && n0 + g.b_off >= k0 + KT - 1;
       if (g.b_mask == MASK_LOWER) plain = plain && k0 + g.b_off >= n0 + TN - 1;
-      auto step = [&](auto masked) {
+      if (!plain) {
+        float* aw = gemm_smem + buf * (BUF / 4);
+        float* bw = aw + ABYTES / 4;
+        // LDS element e of a tile: rows along k hold chunk c of row r at
+        // position c ^ kswz(r); rows along m or n are contiguous.
 #pragma unroll
-        for (int kk = 0; kk < KT / 2; ++kk) {
-          const int k = 2 * kk + (lane >> 5), gk = k0 + k;
-          float a[MB], b[NB];
-#pragma unroll
-          for (int i = 0; i < MB; ++i) {
-            const int m = wm + 32 * i + (lane & 31);
-            a[i] = ak ? as[m * KT + ((((k >> 2) ^ kswz(m))) << 2) + (k & 3)] : as[k * TM + m];
-            if constexpr (decltype(masked)::value) {
-              // branch-free: the value is read, then replaced by zero
-              const int gm = m0 + m;
-              const bool keep = gk < g.K && (g.a_mask == MASK_UPPER   ? gk + g.a_off >= gm
-                                             : g.a_mask == MASK_LOWER ? gm + g.a_off >= gk
-                                                                      : true);
-              a[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, a[i]) & (0u - (uint32_t)keep));
-            }
+        for (int q = 0; q < TM * KT / 256; ++q) {
+          const int e = (int)threadIdx.x + 256 * q;
+          int m, k;
+          if (ak) {
+            m = e / KT;
+            const int w = e % KT;
+            k = ((((w >> 2) ^ kswz(m))) << 2) | (w & 3);
+          } else {
+            k = e / TM;
+            m = e % TM;
           }
-#pragma unroll
-          for (int j = 0; j < NB; ++j) {
-            const int n = wn + 32 * j + (lane & 31);
-            b[j] = bk ? bs[n * KT + ((((k >> 2) ^ kswz(n))) << 2) + (k & 3)] : bs[k * TN + n];
-            if constexpr (decltype(masked)::value) {
-              const int gn = n0 + n;
-              const bool keep = gk < g.K && (g.b_mask == MASK_UPPER   ? gn + g.b_off >= gk
-                                             : g.b_mask == MASK_LOWER ? gk + g.b_off >= gn
-                                                                      : true);
-              b[j] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, b[j]) & (0u - (uint32_t)keep));
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < MB; ++i)
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+          if (!(k0 + k < g.K && keep_a(g.a_mask, g.a_off, m0 + m, k0 + k))) aw[e] = 0.f;
         }
-      };
-      if (plain) step(std::false_type{});
-      else step(std::true_type{});
+#pragma unroll
+        for (int q = 0; q < TN * KT / 256; ++q) {
+          const int e = (int)threadIdx.x + 256 * q;
+          int n, k;
+          if (bk) {
+            n = e / KT;
+            const int w = e % KT;
+            k = ((((w >> 2) ^ kswz(n))) << 2) | (w & 3);
+          } else {
+            k = e / TN;
+            n = e % TN;
+          }
+          if (!(k0 + k < g.K && keep_b(g.b_mask, g.b_off, k0 + k, n0 + n))) bw[e] = 0.f;
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int kk = 0; kk < KT / 2; ++kk) {
+        const int k = 2 * kk + (lane >> 5);
+        float a[MB], b[NB];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const int m = wm + 32 * i + (lane & 31);
+          a[i] = ak ? as[m * KT + ((((k >> 2) ^ kswz(m))) << 2) + (k & 3)] : as[k * TM + m];
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int n = wn + 32 * j + (lane & 31);
+          b[j] = bk ? bs[n * KT + ((((k >> 2) ^ kswz(n))) << 2) + (k & 3)] : bs[k * TN + n];
+        }
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
       // step k0 + KT has landed (own loads) in every wave (barrier); buffer
       // buf is free for the step after it
       __builtin_amdgcn_s_waitcnt(0);

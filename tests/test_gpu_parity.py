@@ -208,7 +208,9 @@ def test_hessian_data_paths_agree_bitwise():
 
 # -------------------------------------------------------------------- prepare
 @pytest.mark.parametrize("d,act_order,n_dead", [(128, False, 0), (256, True, 2), (300, False, 1),
-                                                (513, True, 3), (1000, False, 0)])
+                                                (513, True, 3), (1000, False, 0),
+                                                (2048, True, 2),    # triangular products on 64 x 64 tiles, LDS-direct loads
+                                                (2046, False, 1)])  # the same through the register loader (d % 4 != 0)
 def test_prepare_matches_oracle(d, act_order, n_dead):
     X = S.activations_host(4 * d, d, "normal", outliers=3, gain=5.0, wid=60 + d)
     X[:, np.arange(n_dead) * 7 % d] = 0.0
