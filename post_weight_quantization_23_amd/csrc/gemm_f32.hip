@@ -94,6 +94,56 @@ struct GemmPair {
   int tiles0;   // tiles of g[0]; workgroups from here on belong to g[1]
 };
 
+// C = alpha * acc (+ beta * C) for one wave's MB x NB blocks of 32 x 32 at
+// (r0, c0); lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] of a block.
+// When the blocks lie wholly inside C all their old values are loaded before
+// any is used (one memory round trip, not one per element); otherwise each
+// element is bounds-tested.
+template <int MB, int NB>
+GPTQ_DEV void store_acc(const GemmArgs& g, const floatx16 (&acc)[MB][NB], int r0, int c0, int lane) {
+  auto at = [&](int i, int j, int v) {
+    return g.C + (int64_t)(r0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3)) * g.ldc + c0 + 32 * j +
+           (lane & 31);
+  };
+  if (r0 + 32 * MB <= g.M && c0 + 32 * NB <= g.N) {
+    float old[MB][NB][16];
+    if (g.beta != 0.f) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) old[i][j][v] = *at(i, j, v);
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float out = g.alpha * acc[i][j][v];
+          if (g.beta != 0.f) out = __builtin_fmaf(g.beta, old[i][j][v], out);
+          *at(i, j, v) = out;
+        }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int col = c0 + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = r0 + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < g.M && col < g.N) {
+          float out = g.alpha * acc[i][j][v];
+          if (g.beta != 0.f) out = __builtin_fmaf(g.beta, *at(i, j, v), out);
+          *at(i, j, v) = out;
+        }
+      }
+    }
+}
+
 template <int TM, int TN, int KT>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmPair pr) {
   constexpr int WM = TM / 2, WN = TN / 2;   // per-wave tile
@@ -241,23 +291,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmPair pr) {
     }
   }
 
-  // ---- epilogue: lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] ----
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = n0 + wn + 32 * j + (lane & 31);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < g.M && col < g.N) {
-          float* p = g.C + (int64_t)row * g.ldc + col;
-          float out = g.alpha * acc[i][j][v];
-          if (g.beta != 0.f) out = __builtin_fmaf(g.beta, *p, out);
-          *p = out;
-        }
-      }
-    }
+  store_acc<MB, NB>(g, acc, m0 + wm, n0 + wn, lane);
 }
 
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -381,25 +415,38 @@ GPTQ_DEV void gemm_steps_dma(const GemmArgs& g, int m0, int n0, int k_lo, int k_
         }
         __syncthreads();
       }
-#pragma unroll
-      for (int kk = 0; kk < KT / 2; ++kk) {
+      // Operands of pair kk + 1 are read from LDS while the MFMAs of pair kk
+      // run (two register sets); the scheduling groups keep that order.
+      float a[2][MB], b[2][NB];
+      auto rd = [&](int kk, int sl) {
         const int k = 2 * kk + (lane >> 5);
-        float a[MB], b[NB];
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           const int m = wm + 32 * i + (lane & 31);
-          a[i] = ak ? as[m * KT + ((((k >> 2) ^ kswz(m))) << 2) + (k & 3)] : as[k * TM + m];
+          a[sl][i] = ak ? as[m * KT + ((((k >> 2) ^ kswz(m))) << 2) + (k & 3)] : as[k * TM + m];
         }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           const int n = wn + 32 * j + (lane & 31);
-          b[j] = bk ? bs[n * KT + ((((k >> 2) ^ kswz(n))) << 2) + (k & 3)] : bs[k * TN + n];
+          b[sl][j] = bk ? bs[n * KT + ((((k >> 2) ^ kswz(n))) << 2) + (k & 3)] : bs[k * TN + n];
         }
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < KT / 2; ++kk) {
+        const int cur = kk & 1;
+        if (kk + 1 < KT / 2) rd(kk + 1, cur ^ 1);
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
           for (int j = 0; j < NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[cur][i], b[cur][j], acc[i][j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (MB + NB), 0);   // LDS reads of pairs 0 and 1
+#pragma unroll
+      for (int kk = 0; kk < KT / 2; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MB * NB, 0);        // MFMAs of pair kk
+        if (kk + 2 < KT / 2) __builtin_amdgcn_sched_group_barrier(0x100, MB + NB, 0);   // reads of kk + 2
       }
       // step k0 + KT has landed (own loads) in every wave (barrier); buffer
       // buf is free for the step after it
@@ -444,23 +491,7 @@ __global__ __launch_bounds__(256) void gemm_f32_dma_kernel(GemmPair pr) {
 
   gemm_steps_dma<TM, TN, KT>(g, m0, n0, k_lo, k_hi, wm, wn, acc);
 
-  // ---- epilogue: lane holds D[8*(v/4) + 4*(lane/32) + v%4][lane%32] ----
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int col = n0 + wn + 32 * j + (lane & 31);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < g.M && col < g.N) {
-          float* p = g.C + (int64_t)row * g.ldc + col;
-          float out = g.alpha * acc[i][j][v];
-          if (g.beta != 0.f) out = __builtin_fmaf(g.beta, *p, out);
-          *p = out;
-        }
-      }
-    }
+  store_acc<MB, NB>(g, acc, m0 + wm, n0 + wn, lane);
 }
 
 // Small products (few 64 x 64 tiles, K <= 512): 32 x 32 output tiles, the
@@ -539,17 +570,9 @@ __global__ __launch_bounds__(256) void gemm_f32_small_kernel(GemmPair pr) {
   if (wave > 0) return;
 #pragma unroll
   for (int w = 0; w < 3; ++w) acc += red[w][lane];
-  // lane holds D[8*(v/4) + 4*h + v%4][li]
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = m0 + 8 * (v >> 2) + 4 * h + (v & 3);
-    if (row < g.M && n < g.N) {
-      float* p = g.C + (int64_t)row * g.ldc + n;
-      float out = g.alpha * acc[v];
-      if (g.beta != 0.f) out = __builtin_fmaf(g.beta, *p, out);
-      *p = out;
-    }
-  }
+  floatx16 tile[1][1];
+  tile[0][0] = acc;
+  store_acc<1, 1>(g, tile, m0, n0, lane);
 }
 
 // Workgroups of a problem: every tile, or with upper_only (M == N, square
