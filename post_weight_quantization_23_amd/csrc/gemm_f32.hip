@@ -628,8 +628,7 @@ void launch_tile(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
 }
 
 void launch_dispatch(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
-  // 128 x 128 tiles when that already gives enough workgroups, else 64 x 64;
-  // problems too small to fill the chip with 64 x 64 tiles (and K <= 512) go
+  // Problems too small to fill the chip with 64 x 64 tiles (and K <= 512) go
   // to the small-product kernel.
   const int64_t t128 = tiles_of<128, 128, 32>(g0) + (g1 ? tiles_of<128, 128, 32>(*g1) : 0);
   const int64_t t64 = tiles_of<64, 64, 32>(g0) + (g1 ? tiles_of<64, 64, 32>(*g1) : 0);
@@ -644,7 +643,15 @@ void launch_dispatch(const GemmArgs& g0, const GemmArgs* g1, hipStream_t s) {
     if (t0 + t1 > 0) hipLaunchKernelGGL(gemm_f32_small_kernel, dim3((unsigned)(t0 + t1)), dim3(256), 0, s, pr);
     return;
   }
-  if (t128 >= 480) {
+  // Tile size from the rounds of workgroups the 256 CUs run: a CU's time
+  // follows the most tiles any CU gets, ceil(tiles / 256).  128 x 128 tiles
+  // do a quarter of the work of four 64 x 64 tiles at about 10 % less cost
+  // per flop, but leave more of the last round idle; they are taken when
+  // their rounds, in 64 x 64 units, cost no more than 1.1 times the 64 x 64
+  // rounds, and not when every CU would hold a single tile (one wave per
+  // SIMD, nothing to hide the LDS and memory latency).
+  const int64_t r128 = (t128 + 255) / 256, r64 = (t64 + 255) / 256;
+  if (r128 >= 2 && 40 * r128 <= 11 * r64) {
     launch_tile<128, 128, 32>(g0, g1, s);
   } else {
     launch_tile<64, 64, 32>(g0, g1, s);
