@@ -716,6 +716,34 @@ def bench_sweep(args) -> int:
     return 0
 
 
+def library_reference(X, d: int, n_tok: int, reps: int = 3):
+    """The vendor library's product X^T X on the same activations: torch.mm
+    (hipBLASLt) of the transposed copy and X, the full d x d product in the
+    activations' 16-bit type with fp32 accumulation, timed back to back after
+    the benchmark's own timed region.  Context for the Hessian's rate: the
+    library computes both triangles, the SYRK only the upper one."""
+    import torch
+    if X.dtype not in (torch.bfloat16, torch.float16):
+        return None
+    Xt = X.t().contiguous()
+    out = torch.empty((d, d), dtype=X.dtype, device=X.device)
+    torch.mm(Xt, X, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(Xt, X, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del Xt, out
+    torch.cuda.empty_cache()
+    full = 2.0 * d * d * n_tok
+    return {"what": "torch.mm(X^T, X) (hipBLASLt): the full d x d product, 16-bit output, fp32 accumulation",
+            "ms": ms, "tflops_full_product": full / (ms / 1e3) / 1e12,
+            "tflops_upper_triangle_equiv": d * (d + 1) * n_tok / (ms / 1e3) / 1e12}
+
+
 def bench_hessian(args) -> int:
     """gptq_hessian_accumulate alone, back to back, on the workload's X or on
     an X of the same shape filled with uniform random values in [-1, 1) or
@@ -940,6 +968,10 @@ def main(argv=None) -> int:
         "pack": {"bound": "hbm", "achieved": b_pack / (avg["pack"] / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                  "frac": b_pack / (avg["pack"] / 1e3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": b_pack},
     }
+    lib = library_reference(X, d, w.tokens)
+    if lib is not None:
+        lib["hessian_speedup"] = lib["ms"] / avg["hessian"]
+    rec["library_reference"] = lib
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(W, X, w)
