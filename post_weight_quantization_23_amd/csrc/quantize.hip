@@ -106,7 +106,7 @@ GPTQ_DEV void load_w8(const void* W, int wt, int64_t idx, float (&v)[8]) {
 // with 16-byte loads, MODE 2 reads the permutation with 16-byte loads and
 // gathers the eight weights independently.
 template <int MODE>
-__global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp) {
+__global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp, int wvec) {
   const int64_t row = blockIdx.x;
   const int64_t c = a.c;
   float mn = __builtin_inff(), mx = -__builtin_inff();
@@ -122,10 +122,17 @@ __global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp) {
         const int4 p0 = *reinterpret_cast<const int4*>(a.perm + k);
         const int4 p1 = *reinterpret_cast<const int4*>(a.perm + k + 4);
         const int32_t pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
+        bool run = wvec != 0;   // eight consecutive source columns (the identity
+#pragma unroll                  // permutation everywhere): one vector load
         for (int e = 0; e < 8; ++e) {
           src[e] = clamp_col(pr[e], c);
-          v[e] = load_w(a.W, a.wt, row * a.ldw + src[e]);
+          run = run && src[e] == src[0] + e;
+        }
+        if (run && (src[0] & 7) == 0) {
+          load_w8(a.W, a.wt, row * a.ldw + src[0], v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = load_w(a.W, a.wt, row * a.ldw + src[e]);
         }
       }
       floatx4 o[2];
@@ -753,12 +760,15 @@ void launch_quantize(const QuantArgs& a, hipStream_t s) {
   // E: r x SB row-major, the scaled errors of the current super-block
   float* E = reinterpret_cast<float*>(reinterpret_cast<char*>(a.ws) + align256((size_t)r * c * sizeof(float)));
   const int wbytes = a.wt == 0 ? 4 : 2;
-  const bool vec_w = a.perm == nullptr && c % 8 == 0 && (reinterpret_cast<uintptr_t>(a.W) & 15) == 0 &&
-                     (a.ldw * wbytes) % 16 == 0;
+  // rows of W 16-byte aligned: eight consecutive columns starting at a
+  // multiple of 8 are one 16- or 32-byte load
+  const bool rows16 = (reinterpret_cast<uintptr_t>(a.W) & 15) == 0 && (a.ldw * wbytes) % 16 == 0;
+  const bool vec_w = a.perm == nullptr && c % 8 == 0 && rows16;
   const bool vec_p = a.perm != nullptr && c % 8 == 0 && (reinterpret_cast<uintptr_t>(a.perm) & 15) == 0;
-  if (vec_w) hipLaunchKernelGGL((init_kernel<1>), dim3((unsigned)r), dim3(256), 0, s, a, Wp);
-  else if (vec_p) hipLaunchKernelGGL((init_kernel<2>), dim3((unsigned)r), dim3(256), 0, s, a, Wp);
-  else hipLaunchKernelGGL((init_kernel<0>), dim3((unsigned)r), dim3(256), 0, s, a, Wp);
+  const int wv = rows16 ? 1 : 0;
+  if (vec_w) hipLaunchKernelGGL((init_kernel<1>), dim3((unsigned)r), dim3(256), 0, s, a, Wp, wv);
+  else if (vec_p) hipLaunchKernelGGL((init_kernel<2>), dim3((unsigned)r), dim3(256), 0, s, a, Wp, wv);
+  else hipLaunchKernelGGL((init_kernel<0>), dim3((unsigned)r), dim3(256), 0, s, a, Wp, wv);
   hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)((c + 255) / 256)), dim3(256), 0, s, a.perm, c,
                      a.groupsize, a.g_idx);
   BlockArgs b;
