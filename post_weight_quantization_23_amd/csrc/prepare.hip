@@ -28,25 +28,40 @@ constexpr int NB = 128;      // leaf block handled by one workgroup
 constexpr int LDM = NB + 1;  // LDS row stride of the leaf block
 
 // ---------------------------------------------------------------------------
-// Diagonal pass: dead inputs, NaN/Inf check, info reset.  One workgroup.
+// Diagonal pass, one workgroup: dead inputs (H[j][j] == 0 becomes 1), the
+// NaN/Inf check and the info reset, the undamped diagonal for act-order, the
+// identity permutation when perm is given without act-order, and the damping
+// lambda = percdamp * mean(diag) (after the dead inputs' 1s), summed in a
+// fixed order, added to every diagonal entry.  The damping commutes with the
+// symmetric permutation of act-order (it adds the same lambda to every
+// diagonal entry), so it is applied here in both cases.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void diag_dead_kernel(float* H, int64_t d, uint8_t* dead,
-                                                         int32_t* info, float* diag_out) {
+__global__ __launch_bounds__(1024) void diag_prep_kernel(float* H, int64_t d, uint8_t* dead, int32_t* info,
+                                                         float* diag_out, int32_t* perm_identity,
+                                                         float percdamp) {
   __shared__ int bad;
+  __shared__ float part[1024];
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  for (int64_t j = threadIdx.x; j < d; j += blockDim.x) {
+  float sum = 0.f;
+  for (int64_t j = threadIdx.x; j < d; j += 1024) {
     float v = H[j * d + j];
     if (!__builtin_isfinite(v)) atomicOr(&bad, 1);
     const bool dj = (v == 0.0f);
     dead[j] = dj ? 1 : 0;
-    if (dj) {
-      v = 1.0f;
-      H[j * d + j] = 1.0f;
-    }
+    if (dj) v = 1.0f;
     diag_out[j] = v;
+    sum += v;
+    if (perm_identity) perm_identity[j] = (int32_t)j;
   }
+  part[threadIdx.x] = sum;
   __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  const float lam = percdamp * (part[0] / (float)d);
+  for (int64_t j = threadIdx.x; j < d; j += 1024) H[j * d + j] = diag_out[j] + lam;
   if (threadIdx.x == 0) *info = bad ? -1 : 0;
 }
 
@@ -83,11 +98,6 @@ __global__ __launch_bounds__(256) void rank_kernel(const float* diag, int64_t d,
   if (wave == 0 && i < d) perm[part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = (int32_t)i;
 }
 
-__global__ void identity_perm_kernel(int32_t* perm, int64_t d) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < d) perm[i] = (int32_t)i;
-}
-
 // dst[a][b] = src[min(pa,pb)][max(pa,pb)] for a <= b (upper triangle of the
 // symmetrically permuted matrix).  One row a per blockIdx.y.
 __global__ __launch_bounds__(256) void permute_upper_kernel(const float* src, int64_t d,
@@ -101,21 +111,6 @@ __global__ __launch_bounds__(256) void permute_upper_kernel(const float* src, in
   }
 }
 
-// lambda = percdamp * mean(diag), summed in a fixed order; H[j][j] += lambda.
-__global__ __launch_bounds__(1024) void damp_kernel(float* H, int64_t d, float percdamp) {
-  __shared__ float part[1024];
-  float s = 0.f;
-  for (int64_t j = threadIdx.x; j < d; j += 1024) s += H[j * d + j];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-    __syncthreads();
-  }
-  const float lam = percdamp * (part[0] / (float)d);
-  for (int64_t j = threadIdx.x; j < d; j += 1024) H[j * d + j] += lam;
-}
-
 __global__ __launch_bounds__(256) void copy_block_kernel(const float* src, float* dst, int64_t ld,
                                                          int rows, int cols) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -124,10 +119,23 @@ __global__ __launch_bounds__(256) void copy_block_kernel(const float* src, float
   dst[r * ld + c] = src[r * ld + c];
 }
 
+// Zeros strictly below the diagonal, one row per blockIdx.y; rows of a d with
+// d % 4 == 0 start 16-byte aligned and take four columns per thread.
 __global__ __launch_bounds__(256) void zero_lower_kernel(float* H, int64_t d) {
   const int64_t r = blockIdx.y;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < r; c += (int64_t)gridDim.x * 256)
-    H[r * d + c] = 0.f;
+  float* row = H + r * d;
+  if ((d & 3) == 0) {
+    const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t c = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); c < r; c += 4 * (int64_t)gridDim.x * 256) {
+      if (c + 4 <= r) {
+        *reinterpret_cast<floatx4*>(row + c) = z;
+      } else {
+        for (int64_t e = c; e < r; ++e) row[e] = 0.f;
+      }
+    }
+  } else {
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < r; c += (int64_t)gridDim.x * 256) row[c] = 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -506,8 +514,8 @@ void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t*
   const size_t mat = (size_t)d * (size_t)d * sizeof(float);
   float* Wk = reinterpret_cast<float*>(ws);
   float* diag = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((mat + 255) / 256) * 256);
-  hipLaunchKernelGGL(diag_dead_kernel, dim3(1), dim3(1024), 0, s, H, d, dead, info, diag);
-  const unsigned gb = (unsigned)((d + 255) / 256);
+  hipLaunchKernelGGL(diag_prep_kernel, dim3(1), dim3(1024), 0, s, H, d, dead, info, diag,
+                     act_order ? nullptr : perm, percdamp);
   if (act_order) {
     hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((d + 63) / 64)), dim3(256), 0, s, (const float*)diag, d, perm);
     const unsigned gx = (unsigned)std::min<int64_t>((d + 255) / 256, 64);
@@ -516,13 +524,10 @@ void launch_prepare(float* H, int64_t d, float percdamp, int act_order, int32_t*
     const int64_t cnt = d * d;
     hipLaunchKernelGGL(copy_block_kernel, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, s,
                        (const float*)Wk, H, d, (int)d, (int)d);
-  } else if (perm != nullptr) {
-    hipLaunchKernelGGL(identity_perm_kernel, dim3(gb), dim3(256), 0, s, perm, d);
   }
-  hipLaunchKernelGGL(damp_kernel, dim3(1), dim3(1024), 0, s, H, d, percdamp);
   factor_rec(H, Wk, d, 0, d, info, s);
-  const unsigned gx = (unsigned)std::min<int64_t>((d + 255) / 256, 64);
-  hipLaunchKernelGGL(zero_lower_kernel, dim3(gx, (unsigned)d), dim3(256), 0, s, H, d);
+  const unsigned gz = (unsigned)std::min<int64_t>((d + 1023) / 1024, 64);
+  hipLaunchKernelGGL(zero_lower_kernel, dim3(gz, (unsigned)d), dim3(256), 0, s, H, d);
 }
 
 }  // namespace gptq
