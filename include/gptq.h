@@ -60,7 +60,7 @@ typedef enum GPTQ_ENUM_BASE {
   GPTQ_EDTYPE = 2,        /* dtype not supported by this call                 */
   GPTQ_ESHAPE = 3,        /* inconsistent sizes / leading dimensions           */
   GPTQ_EALIGN = 4,        /* a pointer or leading dimension is misaligned      */
-  GPTQ_EUNSUPPORTED = 5,  /* valid request outside what this build supports    */
+  GPTQ_EUNSUPPORTED = 5,  /* valid request outside what the library supports */
   GPTQ_EWORKSPACE = 6,    /* workspace missing or smaller than the query says */
   GPTQ_EHIP = 7           /* a HIP launch failed                               */
 } gptq_status;
