@@ -104,7 +104,8 @@ GPTQ_DEV void load_w8(const void* W, int wt, int64_t idx, float (&v)[8]) {
 // (a permutation 16-byte aligned, c % 8 == 0): eight consecutive processing
 // columns per thread and step, stored with 16-byte stores; MODE 1 reads W
 // with 16-byte loads, MODE 2 reads the permutation with 16-byte loads and
-// gathers the eight weights independently.
+// gathers the eight weights independently, or loads them as one vector when
+// they are eight consecutive columns of 16-byte aligned rows (wvec).
 template <int MODE>
 __global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp, int wvec) {
   const int64_t row = blockIdx.x;
@@ -122,8 +123,10 @@ __global__ __launch_bounds__(256) void init_kernel(QuantArgs a, float* Wp, int w
         const int4 p0 = *reinterpret_cast<const int4*>(a.perm + k);
         const int4 p1 = *reinterpret_cast<const int4*>(a.perm + k + 4);
         const int32_t pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        bool run = wvec != 0;   // eight consecutive source columns (the identity
-#pragma unroll                  // permutation everywhere): one vector load
+        // eight consecutive source columns (the identity permutation
+        // everywhere) starting at a multiple of 8: one vector load
+        bool run = wvec != 0;
+#pragma unroll
         for (int e = 0; e < 8; ++e) {
           src[e] = clamp_col(pr[e], c);
           run = run && src[e] == src[0] + e;
